@@ -1,0 +1,366 @@
+/*
+ * Oracle for paged MQA logits and one-head indexer scores: a plain, slow,
+ * float64 CPU implementation of the definitions.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this code.  The GPU library
+ * never links it, and this file shares no code, header or table with it.
+ *
+ * Sources (FlashInfer documentation pages):
+ *   [attn_scores]   "flashinfer.attn_scores": the introductory equation
+ *                   logits[t,p] = sum_h w[t,h] * relu(q[t,h] . k_p), the two
+ *                   bullets after it (rectifier per head before the sum; FP8
+ *                   multiplies by the per-token FP32 scale s_p kept in the
+ *                   trailing scale region of each kv_fused block; MXFP4 folds
+ *                   its per-32 block scales into the dequantised values), and
+ *                   the output-contract note (unconditional writes within a
+ *                   row's scheduled extent; rows of requests with
+ *                   seq_lens == 0 are never written).
+ *   [indexer]       "flashinfer.sdsa.indexer_scores": one head, so a score is
+ *                   the plain dot product of a query row and a key; pages of
+ *                   64 keys; scores[q,k] is written for k below the group's
+ *                   length and not beyond.
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *   - the scheduled extent of every row of request b is the request's length
+ *     rounded up to whole 64-token pages, E_b = ceil(L_b/64)*64, clamped to
+ *     max_context; a non-positive length writes nothing;
+ *   - the FP8 query is consumed as decoded e4m3 (the pages give no q scale);
+ *   - e4m3 is OCP E4M3FN, e2m1/e8m0 are OCP MX; the even element of a packed
+ *     FP4 byte is its low nibble;
+ *   - FP8 page layout: 64 tokens x D bytes, then 64 little-endian fp32 scales;
+ *     MXFP4 page layout: 64 tokens x D/2 bytes, then 64 x D/32 e8m0 codes;
+ *   - the block table is int32 [B, bt_stride], page j of request b is
+ *     block_table[b*bt_stride + j]; page i starts at kv + i*page_stride.
+ *
+ * Every arithmetic step is float64 on decoded values.  For each output the
+ * oracle also returns A = s_p * sum_h |w[t,h]| * relu(q[t,h].k_p) (FP8/MXFP4)
+ * or sum_d |q_d k_d| (indexer), the magnitude the parity tolerance scales with.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define TOK_PER_PAGE 64
+
+/* ---------------------------------------------------------------- decoders */
+
+/* OCP E4M3FN: sign, 4-bit exponent (bias 7), 3-bit mantissa; e=15,m=7 is NaN. */
+double oracle_e4m3(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* OCP E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; no NaN/Inf. */
+double oracle_e2m1(uint8_t nib)
+{
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v;
+    if (e == 0)
+        v = 0.5 * m; /* subnormal: m/2 * 2^0 */
+    else
+        v = ldexp((double)(2 + m), e - 2); /* (1 + m/2) * 2^(e-1) */
+    return s ? -v : v;
+}
+
+/* OCP E8M0 scale: 2^(c-127); 0xFF is NaN. */
+double oracle_e8m0(uint8_t c)
+{
+    if (c == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)c - 127);
+}
+
+/* bfloat16: the upper half of an IEEE binary32. */
+double oracle_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double f32_at(const uint8_t* p)
+{
+    float f;
+    memcpy(&f, p, 4);
+    return (double)f;
+}
+
+/* -------------------------------------------------------- extent (reading) */
+
+static int64_t extent_of(int32_t L, int32_t max_context)
+{
+    int64_t E;
+    if (L <= 0)
+        return 0;
+    E = ((int64_t)L + TOK_PER_PAGE - 1) / TOK_PER_PAGE * TOK_PER_PAGE;
+    return E < max_context ? E : max_context;
+}
+
+/* ------------------------------------------------------------- MQA logits */
+
+/*
+ * Shapes (variant 0 = FP8, 1 = MXFP4):
+ *   q        FP8  : e4m3 [B, N, H, D]
+ *            MXFP4: packed e2m1 [B, N, H, D/2], q_sf e8m0 [B, N, H, D/32]
+ *   kv       pages, page i at kv + i*page_stride (layouts above)
+ *   w        fp32 [B*N, H]
+ *   seq_lens int32 [B]; block_table int32 [B, bt_stride]
+ */
+typedef struct {
+    int variant;
+    const uint8_t* q;
+    const uint8_t* q_sf;
+    const uint8_t* kv;
+    int64_t page_stride;
+    const float* w;
+    const int32_t* seq_lens;
+    const int32_t* bt;
+    int64_t bt_stride;
+    int32_t B, N, H, D, max_context;
+} mqa_args;
+
+/* Decoded key vector of KV position p of request b (float64), and its s_p. */
+static double decode_key(const mqa_args* a, int32_t b, int64_t p, double* k)
+{
+    int32_t page = a->bt[(int64_t)b * a->bt_stride + p / TOK_PER_PAGE];
+    int64_t j = p % TOK_PER_PAGE;
+    const uint8_t* pg = a->kv + (int64_t)page * a->page_stride;
+    int D = a->D, d;
+    if (a->variant == 0) {
+        const uint8_t* row = pg + j * D;
+        for (d = 0; d < D; ++d)
+            k[d] = oracle_e4m3(row[d]);
+        return f32_at(pg + (int64_t)TOK_PER_PAGE * D + j * 4); /* s_p */
+    } else {
+        const uint8_t* row = pg + j * (D / 2);
+        const uint8_t* sf = pg + (int64_t)TOK_PER_PAGE * (D / 2) + j * (D / 32);
+        for (d = 0; d < D; ++d) {
+            uint8_t byte = row[d / 2];
+            uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+            k[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / 32]);
+        }
+        return 1.0; /* MXFP4 has no per-position factor */
+    }
+}
+
+/* Decoded query vector for (b, t, h). */
+static void decode_query(const mqa_args* a, int32_t b, int32_t t, int32_t h, double* qv)
+{
+    int D = a->D, d;
+    int64_t qi = (((int64_t)b * a->N + t) * a->H + h);
+    if (a->variant == 0) {
+        const uint8_t* row = a->q + qi * D;
+        for (d = 0; d < D; ++d)
+            qv[d] = oracle_e4m3(row[d]);
+    } else {
+        const uint8_t* row = a->q + qi * (D / 2);
+        const uint8_t* sf = a->q_sf + qi * (D / 32);
+        for (d = 0; d < D; ++d) {
+            uint8_t byte = row[d / 2];
+            uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+            qv[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / 32]);
+        }
+    }
+}
+
+/*
+ * The logit of output row r = b*N + t at KV position p:
+ *   s_p * sum_h w[r,h] * max(0, sum_d q[b,t,h,d] * k_p[d])
+ * with the rectifier applied to each head's score before the weighted sum.
+ * qdec holds the decoded query of (b, t): qdec[h*D + d].
+ */
+static double logit_at(const mqa_args* a, int32_t b, int32_t t, const double* k, double s_p,
+                       const double* qdec, double* amag)
+{
+    int32_t r = b * a->N + t;
+    double acc = 0.0, mag = 0.0;
+    int h, d;
+    for (h = 0; h < a->H; ++h) {
+        double dot = 0.0, relu, wh = (double)a->w[(int64_t)r * a->H + h];
+        for (d = 0; d < a->D; ++d)
+            dot += qdec[(int64_t)h * a->D + d] * k[d];
+        relu = dot > 0.0 ? dot : 0.0;
+        acc += wh * relu;
+        mag += fabs(wh) * relu;
+    }
+    *amag = s_p * mag;
+    return s_p * acc;
+}
+
+/* Decoded query of (b, t) for all heads. */
+static void decode_query_rows(const mqa_args* a, int32_t b, int32_t t, double* qdec)
+{
+    int32_t h;
+    for (h = 0; h < a->H; ++h)
+        decode_query(a, b, t, h, qdec + (int64_t)h * a->D);
+}
+
+/* Dense evaluation: ref/amag are [B*N, max_context] float64, written is u8 of
+ * the same shape (1 where the operation writes the cell).  Cells outside the
+ * written set are left as they are. */
+static int mqa_dense(const mqa_args* a, double* ref, double* amag, uint8_t* written, int nthreads)
+{
+    int32_t b;
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (b = 0; b < a->B; ++b) {
+        int64_t E = extent_of(a->seq_lens[b], a->max_context), p;
+        double* k = (double*)malloc(sizeof(double) * a->D);
+        double* qdec = (double*)malloc(sizeof(double) * (size_t)a->N * a->H * a->D);
+        int32_t t;
+        for (t = 0; t < a->N; ++t)
+            decode_query_rows(a, b, t, qdec + (int64_t)t * a->H * a->D);
+        for (p = 0; p < E; ++p) {
+            double s_p = decode_key(a, b, p, k);
+            for (t = 0; t < a->N; ++t) {
+                int64_t o = ((int64_t)b * a->N + t) * a->max_context + p;
+                double m;
+                ref[o] = logit_at(a, b, t, k, s_p, qdec + (int64_t)t * a->H * a->D, &m);
+                amag[o] = m;
+                written[o] = 1;
+            }
+        }
+        free(k);
+        free(qdec);
+    }
+    return 0;
+}
+
+/* Point evaluation at (rows[i], cols[i]); written[i] says whether the cell is
+ * in the written set (ref/amag are NaN/0 where it is not). */
+static int mqa_points(const mqa_args* a, int64_t npts, const int32_t* rows, const int32_t* cols,
+                      double* ref, double* amag, uint8_t* written, int nthreads)
+{
+    int64_t i;
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads > 0 ? nthreads : 1)
+    for (i = 0; i < npts; ++i) {
+        int32_t r = rows[i], b = r / a->N, t = r % a->N;
+        int64_t p = cols[i], E = extent_of(a->seq_lens[b], a->max_context);
+        if (p < 0 || p >= E) {
+            ref[i] = NAN;
+            amag[i] = 0.0;
+            written[i] = 0;
+        } else {
+            double* k = (double*)malloc(sizeof(double) * a->D);
+            double* qdec = (double*)malloc(sizeof(double) * (size_t)a->H * a->D);
+            double s_p = decode_key(a, b, p, k), m;
+            decode_query_rows(a, b, t, qdec);
+            ref[i] = logit_at(a, b, t, k, s_p, qdec, &m);
+            amag[i] = m;
+            written[i] = 1;
+            free(k);
+            free(qdec);
+        }
+    }
+    return 0;
+}
+
+static int mqa_check(const mqa_args* a)
+{
+    if (a->B < 0 || a->N < 1 || a->H < 1 || a->D < 1 || a->max_context < 0)
+        return -2;
+    if (a->variant == 1 && a->D % 32 != 0)
+        return -2;
+    return 0;
+}
+
+int oracle_mqa_logits(int variant, const uint8_t* q, const uint8_t* q_sf, const uint8_t* kv,
+                      int64_t page_stride, const float* w, const int32_t* seq_lens,
+                      const int32_t* bt, int64_t bt_stride, int32_t B, int32_t N, int32_t H,
+                      int32_t D, int32_t max_context, double* ref, double* amag,
+                      uint8_t* written, int nthreads)
+{
+    mqa_args a = {variant, q, q_sf, kv, page_stride, w, seq_lens, bt, bt_stride,
+                  B, N, H, D, max_context};
+    int rc = mqa_check(&a);
+    if (rc)
+        return rc;
+    return mqa_dense(&a, ref, amag, written, nthreads);
+}
+
+int oracle_mqa_logits_points(int variant, const uint8_t* q, const uint8_t* q_sf,
+                             const uint8_t* kv, int64_t page_stride, const float* w,
+                             const int32_t* seq_lens, const int32_t* bt, int64_t bt_stride,
+                             int32_t B, int32_t N, int32_t H, int32_t D, int32_t max_context,
+                             int64_t npts, const int32_t* rows, const int32_t* cols,
+                             double* ref, double* amag, uint8_t* written, int nthreads)
+{
+    mqa_args a = {variant, q, q_sf, kv, page_stride, w, seq_lens, bt, bt_stride,
+                  B, N, H, D, max_context};
+    int rc = mqa_check(&a);
+    if (rc)
+        return rc;
+    return mqa_points(&a, npts, rows, cols, ref, amag, written, nthreads);
+}
+
+/* ---------------------------------------------------------- indexer scores */
+
+/*
+ * query bf16 [rows, D]; key pages bf16 [64, D] at key_cache + i*page_stride;
+ * block_table int32 [requests, bt_stride]; group g covers rows
+ * row_offsets[g] .. row_offsets[g+1]-1, belongs to request requests[g] and has
+ * context_lengths[g] keys.  scores/amag/written are [rows, max_context].
+ * A group of non-positive length reads nothing (its request is not looked at).
+ */
+int oracle_indexer_scores(const uint16_t* query, int32_t rows, int32_t D, const uint8_t* key_cache,
+                          int64_t page_stride, const int32_t* bt, int64_t bt_stride,
+                          const int32_t* context_lengths, const int32_t* requests,
+                          const int32_t* row_offsets, int32_t groups, int32_t max_context,
+                          double* scores, double* amag, uint8_t* written, int nthreads)
+{
+    int32_t g;
+    (void)nthreads;
+    if (rows < 0 || groups < 0 || D < 1 || max_context < 0)
+        return -2;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (g = 0; g < groups; ++g) {
+        int32_t L = context_lengths[g], r;
+        int64_t k;
+        if (L > max_context)
+            L = max_context;
+        if (L <= 0)
+            continue;
+        for (r = row_offsets[g]; r < row_offsets[g + 1]; ++r) {
+            for (k = 0; k < L; ++k) {
+                int32_t page = bt[(int64_t)requests[g] * bt_stride + k / TOK_PER_PAGE];
+                const uint16_t* key = (const uint16_t*)(key_cache + (int64_t)page * page_stride) +
+                                      (k % TOK_PER_PAGE) * D;
+                double dot = 0.0, mag = 0.0;
+                int d;
+                for (d = 0; d < D; ++d) {
+                    double prod = oracle_bf16(query[(int64_t)r * D + d]) * oracle_bf16(key[d]);
+                    dot += prod;
+                    mag += fabs(prod);
+                }
+                scores[(int64_t)r * max_context + k] = dot;
+                amag[(int64_t)r * max_context + k] = mag;
+                written[(int64_t)r * max_context + k] = 1;
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,336 @@
+"""Seeded synthetic inputs for paged MQA logits and one-head indexer scores.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It only draws random numbers, quantises them to the storage formats
+the operation consumes, and lays them out in pages.  It performs none of the
+scoring arithmetic itself.
+
+Formats (public standards, not taken from any implementation):
+  * e4m3fn  - OCP 8-bit float, bias 7, max 448, NaN = 0x7F/0xFF, no infinity.
+              Encoding uses torch's CPU cast (round to nearest even) after
+              clamping to +-448, because the cast maps out-of-range values to NaN.
+  * e2m1    - OCP MX 4-bit float {0, .5, 1, 1.5, 2, 3, 4, 6} with a sign bit,
+              two per byte, the even element in the low nibble.
+  * e8m0    - OCP MX scale, value 2**(code - 127).
+  * bf16    - top half of an IEEE binary32, round to nearest even (torch cast).
+
+Workloads follow the paged MQA logits page of the FlashInfer documentation
+(flashinfer.attn_scores, introduction and output-contract note) and the
+indexer_scores page (flashinfer.sdsa.indexer_scores, parameter list): pages of
+64 tokens, a block table of int32 page ids per request, per-token FP8 scales in
+a trailing region of each page, MXFP4 block scales per 32 elements.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+PAGE = 64  # tokens per KV page
+INT32_MAX = 2**31 - 1
+
+# --------------------------------------------------------------------------
+# quantisers
+# --------------------------------------------------------------------------
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint8 e4m3fn codes (RNE, saturating at +-448)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp_(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def encode_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bf16 bit patterns (RNE)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def quantize_fp8_per_tensor(x: np.ndarray) -> np.ndarray:
+    """Per-tensor e4m3 quantisation: scale = amax/448 (scale itself is dropped)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    s = amax / 448.0 if amax > 0 else 1.0
+    return encode_e4m3(x / np.float32(s))
+
+
+def quantize_fp8_per_token(x: np.ndarray):
+    """Per-row e4m3 quantisation.  Returns (codes uint8 [..., D], scales f32 [...])."""
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    s[s == 0] = 1.0
+    return encode_e4m3(x / s[..., None]), s
+
+
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+# At a tie the even code wins: for each midpoint, True when the upper neighbour
+# has the even code (so a tie rounds up).
+_E2M1_TIE_UP = np.array([False, True, False, True, False, True, False])
+
+
+def quantize_mxfp4(x: np.ndarray):
+    """OCP MX quantisation with 32-element blocks along the last axis.
+
+    shared exponent = floor(log2(amax)) - 2 (e2m1's largest exponent is 2),
+    elements rounded to nearest even on the e2m1 grid and clamped to +-6.
+    Returns (packed uint8 [..., D/2], scale codes uint8 [..., D/32]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    xb = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.max(np.abs(xb), axis=-1)
+    _, e = np.frexp(amax)  # amax = m * 2**e, m in [0.5, 1)
+    shared = np.where(amax > 0, e.astype(np.int32) - 1 - 2, 0)
+    code = np.clip(shared + 127, 1, 254).astype(np.int32)
+    scale = np.ldexp(np.float32(1.0), code - 127).astype(np.float32)
+    v = np.abs(xb) / scale[..., None]
+    idx = np.zeros(v.shape, dtype=np.uint8)
+    for mid, up in zip(_E2M1_MIDS, _E2M1_TIE_UP):
+        idx += (v >= mid) if up else (v > mid)
+    nib = idx | (np.signbit(xb).astype(np.uint8) << 3)
+    nib = nib.reshape(x.shape)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, code.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# paged MQA logits inputs
+# --------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class MqaInputs:
+    variant: str  # "fp8" or "mxfp4"
+    batch: int
+    next_n: int
+    num_heads: int
+    head_dim: int
+    max_context: int
+    q: np.ndarray  # fp8: u8 [B,N,H,D]; mxfp4: u8 [B,N,H,D/2]
+    q_sf: Optional[np.ndarray]  # mxfp4: u8 [B,N,H,D/32]; fp8: None
+    kv: np.ndarray  # u8 [num_pages, page_stride]
+    page_stride: int
+    weights: np.ndarray  # f32 [B*N, H]
+    seq_lens: np.ndarray  # i32 [B]
+    block_table: np.ndarray  # i32 [B, W]
+    out_dtype: str  # "f32" or "bf16"
+    name: str = ""
+
+    @property
+    def num_pages(self) -> int:
+        return self.kv.shape[0]
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.next_n
+
+    def kv_positions(self) -> int:
+        return int(np.minimum(np.maximum(self.seq_lens, 0), self.max_context).sum())
+
+
+def page_bytes(variant: str, head_dim: int) -> int:
+    """Minimum bytes of one page: 64 tokens of keys, then their scales."""
+    if variant == "fp8":
+        return PAGE * head_dim + PAGE * 4
+    return PAGE * (head_dim // 2) + PAGE * (head_dim // 32)
+
+
+def _fill_pages(rng, variant, num_pages, head_dim, page_stride, chunk=2048):
+    """Every token slot of every page (tails included) holds valid data."""
+    kv = np.zeros((num_pages, page_stride), dtype=np.uint8)
+    kbytes = PAGE * head_dim if variant == "fp8" else PAGE * head_dim // 2
+    for p0 in range(0, num_pages, chunk):
+        p1 = min(num_pages, p0 + chunk)
+        k = rng.standard_normal((p1 - p0, PAGE, head_dim), dtype=np.float32)
+        if variant == "fp8":
+            codes, s = quantize_fp8_per_token(k)
+            kv[p0:p1, :kbytes] = codes.reshape(p1 - p0, -1)
+            kv[p0:p1, kbytes:kbytes + PAGE * 4] = s.view(np.uint8).reshape(p1 - p0, -1)
+        else:
+            packed, sf = quantize_mxfp4(k)
+            kv[p0:p1, :kbytes] = packed.reshape(p1 - p0, -1)
+            kv[p0:p1, kbytes:kbytes + PAGE * head_dim // 32] = sf.reshape(p1 - p0, -1)
+    return kv
+
+
+def make_mqa_inputs(seq_lens, next_n, *, variant="fp8", num_heads=64, head_dim=128,
+                    max_context=None, bt_width=None, w_std=1.0, seed=0,
+                    full_table=False, extra_pages=0, page_stride=None,
+                    out_dtype=None, name="") -> MqaInputs:
+    """Build one paged MQA logits workload.
+
+    Physical page ids are a random permutation; request b owns the next
+    ceil(L_b/64) of them in order.  Unused block-table entries are -1, unless
+    ``full_table`` is set, in which case the table is a permutation of all
+    pages (every entry a valid id).
+    """
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = int(seq_lens.shape[0])
+    N, H, D = int(next_n), int(num_heads), int(head_dim)
+    tiles = [(int(L) + PAGE - 1) // PAGE if L > 0 else 0 for L in seq_lens]
+    if max_context is None:
+        max_context = max(PAGE, max(tiles + [1]) * PAGE)
+    if bt_width is None:
+        bt_width = max(1, max_context // PAGE)
+    need = sum(tiles)
+    num_pages = B * bt_width if full_table else need + extra_pages
+    num_pages = max(num_pages, 1)
+    if page_stride is None:
+        page_stride = page_bytes(variant, D)
+
+    # draws: q, then weights, then page permutation, then page contents
+    qf = rng.standard_normal((B, N, H, D), dtype=np.float32)
+    if variant == "fp8":
+        q = quantize_fp8_per_tensor(qf)
+        q_sf = None
+    else:
+        q, q_sf = quantize_mxfp4(qf)
+    weights = (rng.standard_normal((B * N, H), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    if full_table:
+        block_table = perm[: B * bt_width].reshape(B, bt_width).copy()
+    else:
+        block_table = np.full((B, bt_width), -1, dtype=np.int32)
+        pos = 0
+        for b, T in enumerate(tiles):
+            T = min(T, bt_width)
+            block_table[b, :T] = perm[pos:pos + T]
+            pos += T
+    kv = _fill_pages(rng, variant, num_pages, D, page_stride)
+    if out_dtype is None:
+        out_dtype = "f32" if variant == "fp8" else "bf16"
+    return MqaInputs(variant, B, N, H, D, int(max_context), q, q_sf, kv, int(page_stride),
+                     weights, seq_lens, block_table, out_dtype, name)
+
+
+# --------------------------------------------------------------------------
+# one-head indexer_scores inputs
+# --------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    query: np.ndarray  # u16 bf16 bits [rows, 128]
+    key_cache: np.ndarray  # u8 [pages, page_stride] (bf16 [64,128] at offset 0)
+    page_stride: int
+    block_table: np.ndarray  # i32 [requests, W]
+    context_lengths: np.ndarray  # i32 [groups]
+    requests: np.ndarray  # i32 [groups]
+    group_row_offsets: Optional[np.ndarray]  # i32 [groups+1] or None (uniform)
+    max_context: int
+    name: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.query.shape[0]
+
+    @property
+    def groups(self) -> int:
+        return self.context_lengths.shape[0]
+
+    def row_offsets(self) -> np.ndarray:
+        if self.group_row_offsets is not None:
+            return self.group_row_offsets
+        G = self.rows // self.groups
+        return np.arange(self.groups + 1, dtype=np.int32) * G
+
+    def kv_positions(self) -> int:
+        return int(np.minimum(np.maximum(self.context_lengths, 0), self.max_context).sum())
+
+
+def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=4096,
+                        group_sizes=None, uniform_group=None, max_len=4096,
+                        zero_group=True, seed=2, page_stride=None, head_dim=128,
+                        name="") -> IndexerInputs:
+    rng = np.random.default_rng(seed)
+    if uniform_group is not None:
+        assert rows % uniform_group == 0
+        sizes = [uniform_group] * (rows // uniform_group)
+    elif group_sizes is not None:
+        sizes = list(group_sizes)
+    else:
+        sizes, left = [], rows
+        while left > 0:
+            g = int(min(int(rng.integers(1, 9)), left))
+            sizes.append(g)
+            left -= g
+    assert sum(sizes) == rows and all(1 <= g <= 8 for g in sizes)
+    groups = len(sizes)
+    num_pages = num_requests * bt_width
+    if page_stride is None:
+        page_stride = PAGE * head_dim * 2
+    q = encode_bf16(rng.standard_normal((rows, head_dim), dtype=np.float32))
+    keys = encode_bf16(rng.standard_normal((num_pages, PAGE, head_dim), dtype=np.float32))
+    key_cache = np.zeros((num_pages, page_stride), dtype=np.uint8)
+    key_cache[:, : PAGE * head_dim * 2] = keys.view(np.uint8).reshape(num_pages, -1)
+    block_table = rng.permutation(num_pages).astype(np.int32).reshape(num_requests, bt_width)
+    lengths = rng.integers(0, max_len + 1, size=groups).astype(np.int32)
+    reqs = rng.integers(0, num_requests, size=groups).astype(np.int32)
+    if zero_group:
+        zg = int(rng.integers(0, groups))
+        lengths[zg] = 0
+        reqs[zg] = INT32_MAX  # a 0-length group reads nothing; any value is allowed
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    return IndexerInputs(q, key_cache, int(page_stride), block_table, lengths, reqs,
+                         None if uniform_group is not None else offs, int(max_context), name)
+
+
+# --------------------------------------------------------------------------
+# named workloads
+# --------------------------------------------------------------------------
+
+SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5}
+
+
+def _lens(name, rng):
+    if name == "decode_fp8":
+        u = rng.uniform(math.log(1024), math.log(32768), size=64)
+        return np.rint(np.exp(u)).astype(np.int32)
+    if name == "verify_fp8":
+        return rng.integers(4096, 65536 + 1, size=128).astype(np.int32)
+    if name == "mxfp4":
+        return rng.integers(16384, 131072 + 1, size=64).astype(np.int32)
+    raise KeyError(name)
+
+
+def make_config(name: str, seed: Optional[int] = None, **overrides):
+    """The five named workloads.
+
+    tiny_fp8     B=2, next_n=1, seq_lens {37, 200}, 8 pages, block table a
+                 permutation of all 8, fp32 out [2, 256]
+    indexer_bf16 24 rows in groups of 1..8 over 6 requests, bf16 keys
+                 [384, 64, 128], one zero-length group, fp32 scores [24, 4096]
+    decode_fp8   B=64, next_n=1, seq_lens log-uniform in 1K..32K, w ~ N(0, 0.1^2)
+    verify_fp8   B=128, next_n=4, seq_lens uniform in 4K..64K, w ~ N(0, 0.1^2)
+    mxfp4        B=64, next_n=2, seq_lens uniform in 16K..128K, bf16 out
+    """
+    if seed is None:
+        seed = SEEDS[name]
+    if name == "tiny_fp8":
+        kw = dict(seq_lens=[37, 200], next_n=1, max_context=256, bt_width=4,
+                  full_table=True, w_std=1.0)
+    elif name == "indexer_bf16":
+        kw = dict()
+        kw.update(overrides)
+        return make_indexer_inputs(seed=seed, name=name, **kw)
+    elif name in ("decode_fp8", "verify_fp8", "mxfp4"):
+        lens = _lens(name, np.random.default_rng(seed + 1000))
+        if name == "decode_fp8":
+            kw = dict(seq_lens=lens, next_n=1, max_context=32768, bt_width=512, w_std=0.1)
+        elif name == "verify_fp8":
+            kw = dict(seq_lens=lens, next_n=4, max_context=65536, bt_width=1024, w_std=0.1)
+        else:
+            kw = dict(seq_lens=lens, next_n=2, max_context=131072, bt_width=2048, w_std=1.0,
+                      variant="mxfp4")
+    else:
+        raise KeyError(name)
+    kw.update(overrides)
+    return make_mqa_inputs(seed=seed, name=name, **kw)

@@ -1,0 +1,193 @@
+"""Helpers shared by the tests: golden-fixture builders, independent decoders
+(numpy/torch library casts, not the oracle's) and the parity comparison."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# OCP MX e2m1 magnitudes by 3-bit code (sign is bit 3), from the format table.
+E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+F32_SENTINEL = 0x7FC0FFEE  # a NaN payload no finite write produces
+BF16_SENTINEL = 0x7FC1
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------- independent decoders
+
+
+def np_e4m3(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def np_e8m0(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e8m0fnu).to(torch.float64).numpy()
+
+
+def np_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def np_e2m1_unpack(packed):
+    """u8 [..., D/2] -> float64 [..., D], even element in the low nibble."""
+    lo = packed & 15
+    hi = packed >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(packed.shape[:-1] + (packed.shape[-1] * 2,))
+    mag = E2M1_TABLE[nib & 7]
+    return np.where(nib & 8, -mag, mag)
+
+
+def e2m1_code(v):
+    mag = abs(v)
+    idx = int(np.nonzero(E2M1_TABLE == mag)[0][0])
+    return idx | (8 if v < 0 else 0)
+
+
+def decode_keys(inp):
+    """Per request: (k float64 [E_b, D], s float64 [E_b]) over the written extent."""
+    out = []
+    D = inp.head_dim
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        E = 0 if L <= 0 else min((L + 63) // 64 * 64, inp.max_context)
+        ks, ss = [], []
+        for j in range(E // 64):
+            pg = inp.kv[inp.block_table[b, j]]
+            if inp.variant == "fp8":
+                ks.append(np_e4m3(pg[: 64 * D].reshape(64, D)))
+                ss.append(pg[64 * D: 64 * D + 256].view(np.float32).astype(np.float64))
+            else:
+                vals = np_e2m1_unpack(pg[: 64 * D // 2].reshape(64, D // 2))
+                sf = np_e8m0(pg[64 * D // 2: 64 * D // 2 + 64 * D // 32].reshape(64, D // 32))
+                ks.append(vals * np.repeat(sf, 32, axis=1))
+                ss.append(np.ones(64))
+        out.append((np.concatenate(ks) if ks else np.zeros((0, D)),
+                    np.concatenate(ss) if ss else np.zeros(0)))
+    return out
+
+
+def decode_queries(inp):
+    """float64 [B, N, H, D]."""
+    if inp.variant == "fp8":
+        return np_e4m3(inp.q)
+    vals = np_e2m1_unpack(inp.q)
+    sf = np_e8m0(inp.q_sf)
+    return vals * np.repeat(sf, 32, axis=-1)
+
+
+def flip_key_signs(inp):
+    """A copy of ``inp`` whose key values are negated (scales unchanged)."""
+    import copy
+    out = copy.copy(inp)
+    kv = inp.kv.copy()
+    D = inp.head_dim
+    if inp.variant == "fp8":
+        kv[:, : 64 * D] ^= 0x80
+    else:
+        kv[:, : 64 * D // 2] ^= 0x88
+    out.kv = kv
+    return out
+
+
+# ----------------------------------------------------------- fixture builders
+
+
+def mqa_from_case(case, variant):
+    H, D = 64, 128
+    P = case["num_pages"]
+    stride = synth.page_bytes(variant, D)
+    kv = np.zeros((P, stride), dtype=np.uint8)
+    bt = np.array([case["block_table"]], dtype=np.int32)
+    w = np.zeros((1, H), dtype=np.float32)
+    if variant == "fp8":
+        qf = np.zeros((1, 1, H, D), dtype=np.float32)
+        for hd in case["heads"]:
+            w[0, hd["h"]] = hd["w"]
+            for d, v in hd["q"].items():
+                qf[0, 0, hd["h"], int(d)] = v
+        q = synth.encode_e4m3(qf)
+        assert np.array_equal(np_e4m3(q), qf.astype(np.float64)), "fixture value not exact in e4m3"
+        q_sf = None
+        kv[:, 64 * D: 64 * D + 256] = np.ones((P, 64), dtype=np.float32).view(np.uint8)
+        for tk in case["tokens"]:
+            p = tk["pos"]
+            page, slot = case["block_table"][p // 64], p % 64
+            kf = np.zeros(D, dtype=np.float32)
+            for d, v in tk["k"].items():
+                kf[int(d)] = v
+            codes = synth.encode_e4m3(kf)
+            assert np.array_equal(np_e4m3(codes), kf.astype(np.float64))
+            kv[page, slot * D:(slot + 1) * D] = codes
+            kv[page, 64 * D + 4 * slot: 64 * D + 4 * slot + 4] = np.array(
+                [tk["s"]], dtype=np.float32).view(np.uint8)
+    else:
+        q = np.zeros((1, 1, H, D // 2), dtype=np.uint8)
+        q_sf = np.full((1, 1, H, D // 32), 127, dtype=np.uint8)
+        kv[:, 64 * D // 2: 64 * D // 2 + 64 * D // 32] = 127
+        for hd in case["heads"]:
+            w[0, hd["h"]] = hd["w"]
+            for d, v in hd["q"].items():
+                d = int(d)
+                q[0, 0, hd["h"], d // 2] |= e2m1_code(v) << (4 * (d & 1))
+            for g, c in hd.get("sf", {}).items():
+                q_sf[0, 0, hd["h"], int(g)] = c
+        for tk in case["tokens"]:
+            p = tk["pos"]
+            page, slot = case["block_table"][p // 64], p % 64
+            for d, v in tk["k"].items():
+                d = int(d)
+                kv[page, slot * D // 2 + d // 2] |= e2m1_code(v) << (4 * (d & 1))
+            for g, c in tk.get("sf", {}).items():
+                kv[page, 64 * D // 2 + slot * D // 32 + int(g)] = c
+    L = case["seq_len"]
+    max_context = max(64, (L + 63) // 64 * 64)
+    return synth.MqaInputs(variant, 1, 1, H, D, max_context, q, q_sf, kv, stride, w,
+                           np.array([L], dtype=np.int32), bt,
+                           "f32" if variant == "fp8" else "bf16", case["name"])
+
+
+def indexer_from_case(case):
+    D = 128
+    P = case["num_pages"]
+    rows = len(case["rows"])
+    qf = np.zeros((rows, D), dtype=np.float32)
+    for r, row in enumerate(case["rows"]):
+        for d, v in row["q"].items():
+            qf[r, int(d)] = v
+    q = synth.encode_bf16(qf)
+    keys = np.zeros((P, 64, D), dtype=np.float32)
+    for tk in case["tokens"]:
+        p = tk["pos"]
+        page, slot = case["block_table"][p // 64], p % 64
+        for d, v in tk["k"].items():
+            keys[page, slot, int(d)] = v
+    kc = synth.encode_bf16(keys).view(np.uint8).reshape(P, -1).copy()
+    L = case["context_length"]
+    max_context = max(64, (L + 63) // 64 * 64)
+    bt = np.array([case["block_table"]], dtype=np.int32)
+    return synth.IndexerInputs(q, kc, 64 * D * 2, bt, np.array([L], dtype=np.int32),
+                               np.array([0], dtype=np.int32),
+                               np.array([0, rows], dtype=np.int32), max_context, case["name"])
+
+
+# ---------------------------------------------------------------- comparison
+
+
+def extent(L, max_context):
+    return 0 if L <= 0 else min((L + 63) // 64 * 64, max_context)
