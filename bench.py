@@ -1,0 +1,226 @@
+"""Benchmark: FP8 paged MQA logits (H=64, d=128) on one MI355X.
+
+One step = one whole call of the hot path on the synthetic workload: the
+work split (computed on the GPU, either inside the logits kernel or by the
+schedule kernel), then the logits kernel (page gather, FP8 MFMA, per-head
+rectifier, weighted head sum, s_p, store).  Inputs are resident in HBM before
+the timed region.  The KV cache is replicated and rotated so that one step's
+pages are never still in the 256 MB Infinity Cache from the previous one.
+
+Prints one JSON line (rank 0, one GPU).  Usage:
+  python bench.py [--steps K] [--warmup W] [--workload verify_fp8|decode_fp8|mxfp4]
+                  [--mode in_call|schedule] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain copy of known size (counter scale)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV positions/sec and achieved HBM GB/s, fp8 paged MQA logits H=64 d=128"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+WORKLOADS = {
+    "verify_fp8": "B=128, next_n=4, H=64, d=128, page 64, seq_lens uniform 4K..64K, fp32 out",
+    "decode_fp8": "B=64, next_n=1, H=64, d=128, page 64, seq_lens log-uniform 1K..32K, fp32 out",
+    "mxfp4": "B=64, next_n=2, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
+}
+
+
+def algorithmic_bytes_per_position(variant, next_n, out_bytes):
+    """Bytes the method must move per KV position (page-tail padding, query,
+    weight and block-table reads excluded): the key, its scale, one output
+    per query slot."""
+    if variant == "fp8":
+        return 128 + 4 + next_n * out_bytes
+    return 64 + 4 + next_n * out_bytes
+
+
+def cpu_baseline(inp, target_s=12.0):
+    """The oracle (float64, as it stands) on a bounded sample of the same
+    workload: random KV positions, every query slot of each."""
+    import oracle
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(123)
+    lens = np.minimum(np.maximum(inp.seq_lens, 0), inp.max_context).astype(np.int64)
+    cum = np.concatenate([[0], np.cumsum(lens)])
+
+    def sample(npos):
+        f = rng.integers(0, cum[-1], npos)
+        b = np.searchsorted(cum, f, side="right") - 1
+        p = f - cum[b]
+        rows = (b[:, None] * inp.next_n + np.arange(inp.next_n)[None, :]).ravel()
+        cols = np.repeat(p, inp.next_n)
+        return rows, cols
+
+    done, spent = 0, 0.0
+    npos = 256
+    while spent < target_s:
+        rows, cols = sample(npos)
+        t0 = time.perf_counter()
+        oracle.mqa_logits_points_for(inp, rows, cols, nthreads=threads)
+        dt = time.perf_counter() - t0
+        done += npos
+        spent += dt
+        rate = npos / max(dt, 1e-6)
+        npos = int(min(max(rate * (target_s - spent), 256), 4_000_000))
+        if target_s - spent < 0.5:
+            break
+    return {"value": done / spent, "unit": "KV positions/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random KV positions of the workload x all %d query slots, float64 "
+                      "oracle at sampled cells, %.1f s" % (done, inp.next_n, spent)}
+
+
+def copy_calibration(steps):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiler run."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": dt * 1e3,
+                      "gb_per_s": 2 * n / dt / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="verify_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="in_call", choices=["in_call", "schedule"])
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged MQA logits path has no multi-GPU "
+              "mode here (every logit is independent; sharding by request or page range "
+              "needs no collective).  Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    import synth
+    import paged_mqa_logits_02_amd as pm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pm.init(0)
+    inp = synth.make_config(args.workload)
+    variant = 0 if inp.variant == "fp8" else 1
+    out_dtype = torch.float32 if inp.out_dtype == "f32" else torch.bfloat16
+    out_bytes = 4 if out_dtype == torch.float32 else 2
+
+    kv_bytes = inp.kv.nbytes
+    R = args.replicas or max(2, -(-2 * MALL_BYTES // kv_bytes))
+    kv = [torch.from_numpy(inp.kv).to(dev) for _ in range(R)]
+    q = torch.from_numpy(inp.q).to(dev)
+    q_sf = None if inp.q_sf is None else torch.from_numpy(inp.q_sf).to(dev)
+    w = torch.from_numpy(inp.weights).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    outs = [torch.empty((inp.rows, inp.max_context), dtype=out_dtype, device=dev)
+            for _ in range(2)]
+    U = pm.num_units(inp.next_n, variant)
+    sched = torch.empty(pm.schedule_ints(U), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev0=None, ev1=None):
+        s = None
+        if args.mode == "schedule":
+            pm.mqa_logits_schedule(sl, inp.next_n, variant, max_context=inp.max_context,
+                                   num_units=U, out=sched, stream=stream)
+            s = sched
+        if ev0 is not None:
+            ev0.record(stream)
+        if variant == 0:
+            pm.mqa_logits_fp8(q, kv[i % R], w, sl, bt, max_context=inp.max_context,
+                              out=outs[i % 2], schedule_meta=s, stream=stream)
+        else:
+            pm.mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt, max_context=inp.max_context,
+                                out=outs[i % 2], schedule_meta=s, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(K):
+        step(i, starts[i], ends[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg = float(np.mean(kern_ms))
+
+    positions = inp.kv_positions()
+    bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes)
+    alg_bytes = positions * bpp
+    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
+    value = positions * K / (total_ms * 1e-3)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if inp.variant == "fp8" else "fp4",
+        "data": "synthetic",
+        "gb_per_s": alg_bytes * K / (total_ms * 1e-3) / 1e9,
+        "config": {
+            "workload": args.workload,
+            "shape": WORKLOADS[args.workload],
+            "batch": inp.batch, "next_n": inp.next_n, "num_heads": inp.num_heads,
+            "head_dim": inp.head_dim, "max_context": inp.max_context,
+            "kv_positions": positions, "pages": int(inp.num_pages),
+            "schedule": args.mode, "kv_replicas": R, "units": U,
+            "kernel_ms_avg": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
+            "algorithmic_bytes_per_position": bpp,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

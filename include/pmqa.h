@@ -1,0 +1,196 @@
+/*
+ * pmqa.h - paged MQA logits for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpmqa.so.  Operations (FlashInfer documentation pages):
+ *
+ *   "flashinfer.attn_scores", introductory equation:
+ *       logits[t, p] = s_p * sum_h w[t, h] * relu(q[t, h] . k_p)
+ *   with the rectifier applied per head before the weighted sum (so a negative
+ *   weight can make a logit negative).  The FP8 variant multiplies by the
+ *   per-token fp32 scale s_p held in the trailing scale region of each KV page;
+ *   the MXFP4 variant has no s_p (its per-32-element block scales are part of
+ *   the dequantised q and k values).
+ *
+ *   "flashinfer.sdsa.indexer_scores": the one-head case, a plain dot product of
+ *   each query row with each key of its request, for groups of 1..8 query rows.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never reads device memory on the host, never allocates per call,
+ *     never synchronises, and never prints.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the legacy default stream), so a whole call can be
+ *     captured in a HIP graph.
+ *   - Return value: PMQA_OK (0) or a negative pmqa_status.  Invalid arguments
+ *     are rejected on the host before anything is enqueued.  A failed launch
+ *     returns PMQA_ERR_HIP.
+ *   - Device-data preconditions (not checkable without reading the device):
+ *     seq_lens / context_lengths in [0, max_context] (larger values are clamped
+ *     to max_context, negative ones count as 0), page ids below num_pages, and
+ *     request ids below num_requests.  A page id or request id out of range is
+ *     never dereferenced: the outputs that would depend on it are written as
+ *     NaN instead.
+ *   - Pages hold 64 tokens.
+ */
+#ifndef PMQA_H
+#define PMQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PMQA_OK = 0,
+    PMQA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+    PMQA_ERR_SHAPE = -2,       /* a size or stride is out of range              */
+    PMQA_ERR_UNSUPPORTED = -3, /* a valid but unimplemented option              */
+    PMQA_ERR_ALIGN = -4,       /* a pointer or stride is not aligned as needed  */
+    PMQA_ERR_HIP = -6          /* the HIP runtime reported an error             */
+} pmqa_status;
+
+enum { PMQA_F32 = 0, PMQA_BF16 = 1 };               /* output / accumulator dtypes */
+enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_MXFP4 = 1 };
+
+#define PMQA_PAGE_TOKENS 64
+#define PMQA_MAX_BATCH 8192  /* requests per call                       */
+#define PMQA_MAX_NEXT_N 4    /* query tokens per request (next_n)       */
+
+/*
+ * mqa_logits_fp8 - FP8 paged MQA logits.
+ * ("flashinfer.attn_scores": equation, the s_p bullet, the output-contract note.)
+ *
+ *   q            e4m3fn [batch, next_n, num_heads, head_dim], contiguous, 16-B aligned.
+ *                Consumed as decoded e4m3 (no separate query scale).
+ *   kv_fused     num_pages pages; page i starts at kv_fused + i*page_stride bytes
+ *                and holds 64 x head_dim e4m3 key bytes (token-major) followed
+ *                by 64 little-endian fp32 scales s_p.  page_stride >= 64*(head_dim+4),
+ *                a multiple of 16; kv_fused 16-B aligned.
+ *   weights      fp32 [batch*next_n, num_heads], contiguous, 16-B aligned.
+ *   seq_lens     int32 [batch].
+ *   block_table  int32 [batch, bt_stride]; entry j of row b is the page holding
+ *                tokens 64j..64j+63 of request b.  bt_width = usable entries per
+ *                row; bt_width*64 >= max_context.  Entries at or beyond
+ *                ceil(seq_lens[b]/64) are never read.
+ *   out          [batch*next_n, out_row_stride] of out_dtype (PMQA_F32 or PMQA_BF16).
+ *                Row b*next_n+t is written at columns 0 .. E_b-1, where
+ *                E_b = min(ceil(seq_lens[b]/64)*64, max_context) (whole pages,
+ *                unconditionally, no causal or length mask); later columns and
+ *                every row of a request with seq_lens[b] <= 0 are not touched.
+ *                Only columns 0 .. seq_lens[b]-next_n+t of row b*next_n+t are
+ *                meaningful; masking beyond that is the caller's job.
+ *                max_context % 64 == 0, out_row_stride >= max_context.
+ *   acc_dtype    PMQA_F32 (the only accumulator; anything else -> UNSUPPORTED).
+ *   schedule     NULL (the kernel splits the work itself, on the GPU) or a buffer
+ *                filled by mqa_logits_schedule() with the same next_n, variant
+ *                and max_context, valid only while seq_lens is unchanged
+ *                ("flashinfer.attn_scores", Scheduling and Setup, and its warning).
+ *                A schedule built for other arguments is detected on the device
+ *                and ignored.
+ *   Supported: num_heads == 64, head_dim == 128, 1 <= next_n <= 4.
+ */
+int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int32_t num_pages,
+                   const float* weights, const int32_t* seq_lens, const int32_t* block_table,
+                   int64_t bt_stride, int32_t bt_width, int32_t batch, int32_t next_n,
+                   int32_t num_heads, int32_t head_dim, void* out, int64_t out_row_stride,
+                   int32_t max_context, int32_t out_dtype, int32_t acc_dtype,
+                   const int32_t* schedule, void* stream);
+
+/*
+ * mqa_logits_mxfp4 - MXFP4 paged MQA logits (no s_p; block scales folded).
+ * ("flashinfer.attn_scores": equation, the MXFP4 bullet, and the paragraph on
+ * q_sf / sf_vec_size / is_kv_sf_interleaved, two FP4 values per byte, exactly
+ * 64 heads and head_dim 128.)
+ *
+ *   q            packed e2m1 [batch, next_n, 64, 64] (two values per byte, the
+ *                even element in the low nibble), 16-B aligned.
+ *   q_sf         e8m0 [batch, next_n, 64, 128/sf_vec_size]; sf_vec_size == 32.
+ *   is_kv_sf_interleaved  0: each page holds 64 x 64 packed key bytes, then
+ *                64 x 4 e8m0 scale codes (token-major).  1 -> UNSUPPORTED.
+ *   kv_fused     page i at kv_fused + i*page_stride; page_stride >= 4352, a
+ *                multiple of 16.
+ *   out_dtype    PMQA_BF16 (the default of this variant, round to nearest even)
+ *                or PMQA_F32.
+ *   Everything else as in mqa_logits_fp8.
+ */
+int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
+                     int32_t is_kv_sf_interleaved, const void* kv_fused, int64_t page_stride,
+                     int32_t num_pages, const float* weights, const int32_t* seq_lens,
+                     const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                     int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                     void* out, int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
+                     const int32_t* schedule, void* stream);
+
+/*
+ * indexer_scores - one-head BF16 indexer scores.
+ * ("flashinfer.sdsa.indexer_scores": description and parameter list.)
+ *
+ *   query            bf16 [rows, 128], contiguous, 16-B aligned.
+ *   key_cache        bf16 key pages [64, 128]; page i at key_cache + i*page_stride
+ *                    bytes, page_stride >= 16384 and a multiple of 16 (views into
+ *                    a cache that also holds other data per page are fine).
+ *   block_table      int32 [num_requests, bt_stride], bt_width usable entries per
+ *                    row, bt_width*64 >= max_context.
+ *   context_lengths  int32 [groups]: keys of each group.
+ *   requests         int32 [groups]: the block-table row of each group; not read
+ *                    for a group of length <= 0, so any value is allowed there.
+ *   group_row_offsets  NULL: every group has rows/groups consecutive rows (an
+ *                    integer in 1..8).  Otherwise int32 [groups+1], nondecreasing
+ *                    from 0 to rows, each group 1..8 rows (device data: the host
+ *                    cannot check it; a group outside 1..8 rows is skipped).
+ *   scores           fp32 [rows, scores_row_stride]: scores[r, k] for k below the
+ *                    group's length (clamped to max_context) is the dot product
+ *                    of query row r with key k; later entries are not written.
+ *                    max_context % 64 == 0, scores_row_stride >= max_context.
+ */
+int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
+                   int64_t page_stride, int32_t num_pages, const int32_t* block_table,
+                   int64_t bt_stride, int32_t bt_width, int32_t num_requests,
+                   const int32_t* context_lengths, const int32_t* requests, int32_t groups,
+                   const int32_t* group_row_offsets, float* scores, int64_t scores_row_stride,
+                   int32_t max_context, void* stream);
+
+/*
+ * mqa_logits_schedule - the per-call work split, computed on the GPU.
+ * ("flashinfer.attn_scores", Scheduling and Setup: a per-call work assignment
+ * computed on the device, which a caller may build once and pass back.)
+ *
+ * Splits the (request, 64-token page) work items of one call, in request-major
+ * order, into num_units contiguous ranges of near-equal length and writes the
+ * opaque int32 buffer `schedule` of mqa_logits_schedule_ints(num_units)
+ * entries.  num_units in 1 .. 1<<20; 0 means mqa_logits_num_units(current
+ * device, next_n, variant).  The result depends only on seq_lens, batch,
+ * next_n, variant and max_context; it must be rebuilt whenever seq_lens
+ * changes (including on every graph replay).
+ */
+int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,
+                        int32_t max_context, int32_t num_units, int32_t* schedule, void* stream);
+
+/* Number of int32 entries of a schedule buffer for num_units units. */
+int64_t mqa_logits_schedule_ints(int32_t num_units);
+
+/* The unit count a NULL-schedule call of this configuration uses on `device`
+ * (waves resident on the whole GPU); < 0 on error. */
+int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant);
+
+/* Columns written per row for a request of seq_len tokens: ceil(seq_len/64)*64
+ * (0 for seq_len <= 0).  ("flashinfer.attn_scores": padded_seq_len.) */
+int32_t mqa_logits_padded_seq_len(int32_t seq_len, int32_t next_n, int32_t variant);
+
+/* Block-table entries a request of max_seq_len tokens needs: ceil(max_seq_len/64).
+ * ("flashinfer.attn_scores": min_block_table_width.) */
+int32_t mqa_logits_min_block_table_width(int32_t max_seq_len, int32_t next_n, int32_t variant);
+
+/* Loads the code objects on `device` and caches its compute-unit count.  Call
+ * it once per device before capturing a call in a HIP graph.  Idempotent. */
+int mqa_logits_init(int device);
+
+/* A static, human-readable name for a status code. */
+const char* mqa_logits_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMQA_H */

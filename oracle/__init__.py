@@ -57,6 +57,7 @@ def _load():
             lib.oracle_mqa_logits_points.argtypes = [ctypes.c_int, P, P, P, I64, P, P, P, I64,
                                                      I32, I32, I32, I32, I32, I64, P, P,
                                                      P, P, P, ctypes.c_int]
+            lib.oracle_mqa_written.argtypes = [P, I32, I32, I32, P]
             lib.oracle_indexer_scores.argtypes = [P, I32, I32, P, I64, P, I64, P, P, P, I32, I32,
                                                   P, P, P, ctypes.c_int]
             for f in ("oracle_e4m3", "oracle_e2m1", "oracle_e8m0"):
@@ -162,6 +163,17 @@ def mqa_logits_points_for(inp, rows, cols, nthreads=None):
                              inp.weights, inp.seq_lens, inp.block_table, inp.batch,
                              inp.next_n, inp.num_heads, inp.head_dim, inp.max_context,
                              rows, cols, nthreads)
+
+
+def mqa_written(seq_lens, batch, next_n, max_context):
+    """The cells the operation writes, bool [batch*next_n, max_context]."""
+    lib = _load()
+    sl = _c(seq_lens, np.int32)
+    written = np.zeros((batch * next_n, max_context), dtype=np.uint8)
+    rc = lib.oracle_mqa_written(_ptr(sl), batch, next_n, max_context, _ptr(written))
+    if rc != 0:
+        raise ValueError("oracle_mqa_written: bad arguments (%d)" % rc)
+    return written.astype(bool)
 
 
 # ------------------------------------------------------------ indexer scores

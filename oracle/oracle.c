@@ -308,6 +308,24 @@ int oracle_mqa_logits_points(int variant, const uint8_t* q, const uint8_t* q_sf,
     return mqa_points(&a, npts, rows, cols, ref, amag, written, nthreads);
 }
 
+/* The written set alone ([B*N, max_context] u8): cheap, for full-size checks. */
+int oracle_mqa_written(const int32_t* seq_lens, int32_t B, int32_t N, int32_t max_context,
+                       uint8_t* written)
+{
+    int32_t b, t;
+    if (B < 0 || N < 1 || max_context < 0)
+        return -2;
+    for (b = 0; b < B; ++b) {
+        int64_t E = extent_of(seq_lens[b], max_context);
+        for (t = 0; t < N; ++t) {
+            uint8_t* row = written + ((int64_t)b * N + t) * max_context;
+            memset(row, 0, (size_t)max_context);
+            memset(row, 1, (size_t)E);
+        }
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------- indexer scores */
 
 /*

@@ -1,0 +1,262 @@
+"""Paged MQA logits for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libpmqa.so`` (declared in
+``include/pmqa.h``).  Every function here only marshals torch tensors into
+device pointers, sizes and strides and passes torch's current HIP stream; all
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or fails to load, importing this package raises.
+
+Operations (FlashInfer documentation pages):
+  * ``mqa_logits_fp8`` / ``mqa_logits_mxfp4`` - "flashinfer.attn_scores":
+    logits[t, p] = s_p * sum_h w[t, h] * relu(q[t, h] . k_p), rectifier per
+    head before the weighted sum, s_p only for FP8, MXFP4 block scales folded
+    into q and k; output contract of the page's note.
+  * ``indexer_scores`` - "flashinfer.sdsa.indexer_scores": one head, a plain
+    dot product per (query row, key) for groups of 1..8 rows.
+  * ``mqa_logits_schedule`` and the helpers - "flashinfer.attn_scores",
+    Scheduling and Setup.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpmqa.so")
+
+F32, BF16 = 0, 1
+VARIANT_FP8, VARIANT_MXFP4 = 0, 1
+PAGE = 64
+
+_STATUS = {0: "PMQA_OK", -1: "PMQA_ERR_NULL", -2: "PMQA_ERR_SHAPE", -3: "PMQA_ERR_UNSUPPORTED",
+           -4: "PMQA_ERR_ALIGN", -6: "PMQA_ERR_HIP"}
+
+
+class PmqaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, status_string(status)))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpmqa.so is not built (%s); run __graft_entry__.build() or "
+                          "python paged_mqa_logits_02_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.mqa_logits_fp8.argtypes = [P, P, I64, I32, P, P, P, I64, I32, I32, I32, I32, I32, P, I64,
+                                   I32, I32, I32, P, P]
+    lib.mqa_logits_mxfp4.argtypes = [P, P, I32, I32, P, I64, I32, P, P, P, I64, I32, I32, I32,
+                                     I32, I32, P, I64, I32, I32, P, P]
+    lib.indexer_scores.argtypes = [P, I32, I32, P, I64, I32, P, I64, I32, I32, P, P, I32, P, P,
+                                   I64, I32, P]
+    lib.mqa_logits_schedule.argtypes = [P, I32, I32, I32, I32, I32, P, P]
+    lib.mqa_logits_schedule_ints.argtypes = [I32]
+    lib.mqa_logits_schedule_ints.restype = I64
+    lib.mqa_logits_num_units.argtypes = [ctypes.c_int, I32, I32]
+    lib.mqa_logits_num_units.restype = I32
+    lib.mqa_logits_padded_seq_len.argtypes = [I32, I32, I32]
+    lib.mqa_logits_padded_seq_len.restype = I32
+    lib.mqa_logits_min_block_table_width.argtypes = [I32, I32, I32]
+    lib.mqa_logits_min_block_table_width.restype = I32
+    lib.mqa_logits_init.argtypes = [ctypes.c_int]
+    lib.mqa_logits_status_string.argtypes = [ctypes.c_int]
+    lib.mqa_logits_status_string.restype = ctypes.c_char_p
+    for f in ("mqa_logits_fp8", "mqa_logits_mxfp4", "indexer_scores", "mqa_logits_schedule",
+              "mqa_logits_init"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes handle of libpmqa.so."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.mqa_logits_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise PmqaError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype != torch.uint8 and t.element_size() == 1 else t
+
+
+def _rows_of(t: torch.Tensor):
+    """(row stride in elements, row width) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0), t.shape[1]
+
+
+def _pages(t: torch.Tensor):
+    """(page stride in bytes, number of pages) of a paged cache.
+
+    Accepts [pages, bytes] uint8 (pages may be a strided view) or any tensor
+    whose first dimension is the page index and whose page contents are
+    contiguous."""
+    if t.dim() < 2:
+        raise ValueError("a paged cache needs a page dimension")
+    inner = t[0]
+    if not inner.is_contiguous():
+        raise ValueError("page contents must be contiguous")
+    return t.stride(0) * t.element_size(), t.shape[0]
+
+
+# ---------------------------------------------------------------- helpers
+
+
+def init(device=None) -> None:
+    dev = torch.cuda.current_device() if device is None else int(device)
+    _check(_lib.mqa_logits_init(dev), "mqa_logits_init")
+
+
+def num_units(next_n: int, variant: int = VARIANT_FP8, device=None) -> int:
+    dev = torch.cuda.current_device() if device is None else int(device)
+    n = _lib.mqa_logits_num_units(dev, next_n, variant)
+    _check(min(n, 0), "mqa_logits_num_units")
+    return n
+
+
+def padded_seq_len(seq_len: int, next_n: int = 1, variant: int = VARIANT_FP8) -> int:
+    return _lib.mqa_logits_padded_seq_len(seq_len, next_n, variant)
+
+
+def min_block_table_width(max_seq_len: int, next_n: int = 1, variant: int = VARIANT_FP8) -> int:
+    return _lib.mqa_logits_min_block_table_width(max_seq_len, next_n, variant)
+
+
+def schedule_ints(num_units_: int) -> int:
+    return int(_lib.mqa_logits_schedule_ints(num_units_))
+
+
+def mqa_logits_schedule(seq_lens: torch.Tensor, next_n: int, variant: int = VARIANT_FP8, *,
+                        max_context: int, num_units: int = 0, out: torch.Tensor = None,
+                        stream=None) -> torch.Tensor:
+    """Builds the opaque work split on the GPU (int32 tensor).  Valid only
+    while seq_lens is unchanged; pass the same next_n/variant/max_context to
+    the logits call."""
+    if num_units == 0:
+        num_units = globals()["num_units"](next_n, variant, seq_lens.device.index)
+    n = schedule_ints(num_units)
+    if n < 0:
+        raise PmqaError(-2, "mqa_logits_schedule")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
+    elif out.numel() < n or out.dtype != torch.int32:
+        raise ValueError("schedule buffer too small")
+    _check(_lib.mqa_logits_schedule(_ptr(seq_lens), seq_lens.shape[0], next_n, variant,
+                                    max_context, num_units, _ptr(out),
+                                    _stream(stream, seq_lens.device)), "mqa_logits_schedule")
+    return out
+
+
+# ---------------------------------------------------------------- operations
+
+
+def _out_for(out, rows, max_context, dtype, device):
+    if out is None:
+        return torch.empty((rows, max_context), dtype=dtype, device=device)
+    return out
+
+
+def _dtype_code(dtype):
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise ValueError("unsupported output dtype %s" % dtype)
+
+
+def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
+                   max_context=None, out=None, schedule_meta=None,
+                   output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
+    """FP8 paged MQA logits; returns ``out`` [batch*next_n, max_context].
+
+    q [batch, next_n, 64, 128] e4m3 (uint8 or float8_e4m3fn); kv_fused
+    [pages, page_bytes] uint8 (a strided view is fine); weights
+    [batch*next_n, 64] fp32; seq_lens [batch] int32; block_table
+    [batch, width] int32.  Columns at or beyond ceil(seq_len/64)*64 and rows
+    of empty requests are not written (out=None allocates uninitialised
+    memory)."""
+    B, N, H, D = q.shape
+    if next_n is not None and next_n != N:
+        raise ValueError("next_n does not match q")
+    bt_stride, bt_width = _rows_of(block_table)
+    if max_context is None:
+        max_context = out.shape[1] if out is not None else bt_width * PAGE
+    out = _out_for(out, B * N, max_context, output_dtype, q.device)
+    ors, _ = _rows_of(out)
+    ps, npages = _pages(kv_fused)
+    acc = _dtype_code(acc_dtype) if acc_dtype in (torch.float32, torch.bfloat16) else 99
+    _check(_lib.mqa_logits_fp8(_ptr(q), _ptr(kv_fused), ps, npages, _ptr(weights),
+                               _ptr(seq_lens), _ptr(block_table), bt_stride, bt_width, B, N, H,
+                               D, _ptr(out), ors, max_context, _dtype_code(out.dtype), acc,
+                               _ptr(schedule_meta), _stream(stream, q.device)),
+           "mqa_logits_fp8")
+    return out
+
+
+def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=None, *,
+                     sf_vec_size=32, is_kv_sf_interleaved=False, max_context=None, out=None,
+                     schedule_meta=None, output_dtype=torch.bfloat16, stream=None):
+    """MXFP4 paged MQA logits; returns ``out`` [batch*next_n, max_context].
+
+    q [batch, next_n, 64, 64] packed e2m1 uint8; q_sf [batch, next_n, 64, 4]
+    e8m0 uint8; kv_fused [pages, page_bytes] uint8 with 64x64 packed key bytes
+    then 64x4 e8m0 codes per page."""
+    B, N, H, Dh = q.shape
+    if next_n is not None and next_n != N:
+        raise ValueError("next_n does not match q")
+    bt_stride, bt_width = _rows_of(block_table)
+    if max_context is None:
+        max_context = out.shape[1] if out is not None else bt_width * PAGE
+    out = _out_for(out, B * N, max_context, output_dtype, q.device)
+    ors, _ = _rows_of(out)
+    ps, npages = _pages(kv_fused)
+    _check(_lib.mqa_logits_mxfp4(_ptr(q), _ptr(q_sf), sf_vec_size, int(is_kv_sf_interleaved),
+                                 _ptr(kv_fused), ps, npages, _ptr(weights), _ptr(seq_lens),
+                                 _ptr(block_table), bt_stride, bt_width, B, N, H, Dh * 2,
+                                 _ptr(out), ors, max_context, _dtype_code(out.dtype),
+                                 _ptr(schedule_meta), _stream(stream, q.device)),
+           "mqa_logits_mxfp4")
+    return out
+
+
+def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,
+                   group_row_offsets=None, stream=None):
+    """One-head BF16 indexer scores into ``scores`` [rows, max_context] fp32.
+
+    query [rows, 128] bf16; key_cache [pages, 64, 128] bf16 or [pages, bytes]
+    uint8 (pages may be strided views); block_table [requests, width] int32;
+    context_lengths / requests [groups] int32; group_row_offsets optional
+    [groups+1] int32 (None: rows/groups rows per group)."""
+    rows, D = query.shape
+    bt_stride, bt_width = _rows_of(block_table)
+    srs, max_context = _rows_of(scores)
+    ps, npages = _pages(key_cache)
+    _check(_lib.indexer_scores(_ptr(query), rows, D, _ptr(key_cache), ps, npages,
+                               _ptr(block_table), bt_stride, bt_width, block_table.shape[0],
+                               _ptr(context_lengths), _ptr(requests), context_lengths.shape[0],
+                               _ptr(group_row_offsets), _ptr(scores), srs, max_context,
+                               _stream(stream, query.device)), "indexer_scores")
+    return scores

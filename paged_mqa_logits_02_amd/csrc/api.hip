@@ -1,0 +1,299 @@
+// C ABI of libpmqa.so (declared in include/pmqa.h): host-side validation,
+// per-device cached facts, and kernel launches.  No entry point allocates,
+// synchronises or reads device memory.
+#include <mutex>
+
+#include "pmqa.h"
+#include "pmqa_internal.h"
+
+namespace pmqa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool ready = false;
+  int cus = 0;
+  // workgroups per CU for each kernel instance [next_n-1][variant][out]
+  int occ[PMQA_MAX_NEXT_N][2][2] = {};
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+int init_device(int device) {
+  if (device < 0 || device >= kMaxDevices) return PMQA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_dev[device];
+  if (d.ready) return PMQA_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return PMQA_ERR_HIP;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return PMQA_ERR_HIP;
+  int rc = PMQA_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+    rc = PMQA_ERR_HIP;
+  } else {
+    d.cus = prop.multiProcessorCount;
+    for (int n = 1; n <= PMQA_MAX_NEXT_N && rc == PMQA_OK; ++n)
+      for (int v = 0; v < 2 && rc == PMQA_OK; ++v)
+        for (int o = 0; o < 2 && rc == PMQA_OK; ++o) {
+          int blocks = 0;
+          // Occupancy with the LDS of a 4096-request batch; loads the code object.
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  &blocks, mqa_kernel_symbol(n, v, o), kBlockThreads,
+                  (4096 + 1) * sizeof(int)) != hipSuccess) {
+            rc = PMQA_ERR_HIP;
+          }
+          d.occ[n - 1][v][o] = blocks > 0 ? blocks : 1;
+        }
+    hipFuncAttributes attr;
+    if (rc == PMQA_OK && (hipFuncGetAttributes(&attr, schedule_kernel_symbol()) != hipSuccess ||
+                          hipFuncGetAttributes(&attr, indexer_kernel_symbol()) != hipSuccess))
+      rc = PMQA_ERR_HIP;
+  }
+  if (cur != device && hipSetDevice(cur) != hipSuccess) rc = PMQA_ERR_HIP;
+  if (rc == PMQA_OK) d.ready = true;
+  return rc;
+}
+
+int current_device_info(DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PMQA_ERR_HIP;
+  int rc = init_device(dev);
+  if (rc != PMQA_OK) return rc;
+  *out = &g_dev[dev];
+  return PMQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Checks shared by both MQA variants.
+int check_mqa_common(const void* q, const void* kv, int64_t page_stride, int32_t num_pages,
+                     const float* w, const int32_t* seq_lens, const int32_t* bt,
+                     int64_t bt_stride, int32_t bt_width, int32_t batch, int32_t next_n,
+                     void* out, int64_t out_row_stride, int32_t max_context, int64_t min_stride) {
+  if (batch < 0 || batch > PMQA_MAX_BATCH) return PMQA_ERR_SHAPE;
+  if (next_n < 1 || next_n > 64) return PMQA_ERR_SHAPE;
+  if (next_n > PMQA_MAX_NEXT_N) return PMQA_ERR_UNSUPPORTED;
+  if (max_context < 0 || max_context % PMQA_PAGE_TOKENS != 0) return PMQA_ERR_SHAPE;
+  if (batch == 0 || max_context == 0) return PMQA_OK;  // nothing to do (caller checks null)
+  if (!q || !kv || !w || !seq_lens || !bt || !out) return PMQA_ERR_NULL;
+  if (num_pages < 1) return PMQA_ERR_SHAPE;
+  if (page_stride < min_stride) return PMQA_ERR_SHAPE;
+  if (page_stride % 16 != 0) return PMQA_ERR_ALIGN;
+  if (bt_width < 1 || bt_stride < bt_width) return PMQA_ERR_SHAPE;
+  if ((int64_t)bt_width * PMQA_PAGE_TOKENS < max_context) return PMQA_ERR_SHAPE;
+  if (out_row_stride < max_context) return PMQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(w)) return PMQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(seq_lens) | reinterpret_cast<uintptr_t>(bt)) & 3)
+    return PMQA_ERR_ALIGN;
+  return PMQA_OK;
+}
+
+int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride,
+            int32_t num_pages, const float* w, const int32_t* seq_lens, const int32_t* bt,
+            int64_t bt_stride, int32_t batch, int32_t next_n, int variant, void* out,
+            int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
+            const int32_t* schedule, void* stream) {
+  DeviceInfo* d = nullptr;
+  int rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
+  MqaArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.q_sf = static_cast<const uint8_t*>(q_sf);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.page_stride = page_stride;
+  a.w = w;
+  a.seq_lens = seq_lens;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.out = out;
+  a.out_row_stride = out_row_stride;
+  a.schedule = schedule;
+  a.num_pages = num_pages;
+  a.batch = batch;
+  a.max_context = max_context;
+  a.pad_ = 0;
+  const int grid = d->cus * d->occ[next_n - 1][variant][out_dtype];
+  const size_t lds = (size_t)(batch + 1) * sizeof(int);
+  if (launch_mqa(a, next_n, variant, out_dtype, grid, lds, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PMQA_ERR_HIP;
+  return PMQA_OK;
+}
+
+}  // namespace
+}  // namespace pmqa
+
+using namespace pmqa;
+
+extern "C" {
+
+int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int32_t num_pages,
+                   const float* weights, const int32_t* seq_lens, const int32_t* block_table,
+                   int64_t bt_stride, int32_t bt_width, int32_t batch, int32_t next_n,
+                   int32_t num_heads, int32_t head_dim, void* out, int64_t out_row_stride,
+                   int32_t max_context, int32_t out_dtype, int32_t acc_dtype,
+                   const int32_t* schedule, void* stream) {
+  if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
+  if (num_heads != 64 || head_dim != 128) return PMQA_ERR_UNSUPPORTED;
+  if (out_dtype != PMQA_F32 && out_dtype != PMQA_BF16) return PMQA_ERR_UNSUPPORTED;
+  if (acc_dtype != PMQA_F32) return PMQA_ERR_UNSUPPORTED;
+  int rc = check_mqa_common(q, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
+                            bt_stride, bt_width, batch, next_n, out, out_row_stride, max_context,
+                            (int64_t)PMQA_PAGE_TOKENS * (head_dim + 4));
+  if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
+  return run_mqa(q, nullptr, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
+                 bt_stride, batch, next_n, PMQA_VARIANT_FP8, out, out_row_stride, max_context,
+                 out_dtype, schedule, stream);
+}
+
+int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
+                     int32_t is_kv_sf_interleaved, const void* kv_fused, int64_t page_stride,
+                     int32_t num_pages, const float* weights, const int32_t* seq_lens,
+                     const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                     int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                     void* out, int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
+                     const int32_t* schedule, void* stream) {
+  if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
+  if (num_heads != 64 || head_dim != 128) return PMQA_ERR_UNSUPPORTED;
+  if (sf_vec_size != 32 || is_kv_sf_interleaved != 0) return PMQA_ERR_UNSUPPORTED;
+  if (out_dtype != PMQA_F32 && out_dtype != PMQA_BF16) return PMQA_ERR_UNSUPPORTED;
+  int rc = check_mqa_common(q, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
+                            bt_stride, bt_width, batch, next_n, out, out_row_stride, max_context,
+                            (int64_t)PMQA_PAGE_TOKENS * (head_dim / 2 + head_dim / 32));
+  if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
+  if (!q_sf) return PMQA_ERR_NULL;
+  return run_mqa(q, q_sf, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
+                 bt_stride, batch, next_n, PMQA_VARIANT_MXFP4, out, out_row_stride, max_context,
+                 out_dtype, schedule, stream);
+}
+
+int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
+                   int64_t page_stride, int32_t num_pages, const int32_t* block_table,
+                   int64_t bt_stride, int32_t bt_width, int32_t num_requests,
+                   const int32_t* context_lengths, const int32_t* requests, int32_t groups,
+                   const int32_t* group_row_offsets, float* scores, int64_t scores_row_stride,
+                   int32_t max_context, void* stream) {
+  if (rows < 0 || groups < 0 || groups > 65535 || head_dim < 1) return PMQA_ERR_SHAPE;
+  if (head_dim != 128) return PMQA_ERR_UNSUPPORTED;
+  if (max_context < 0 || max_context % PMQA_PAGE_TOKENS != 0) return PMQA_ERR_SHAPE;
+  if (groups > 0 && rows < 1) return PMQA_ERR_SHAPE;
+  int uniform_g = 0;
+  if (!group_row_offsets && groups > 0) {
+    if (rows % groups != 0) return PMQA_ERR_SHAPE;
+    uniform_g = rows / groups;
+    if (uniform_g < 1 || uniform_g > 8) return PMQA_ERR_SHAPE;
+  }
+  if (groups == 0 || max_context == 0) return PMQA_OK;
+  if (!query || !key_cache || !block_table || !context_lengths || !requests || !scores)
+    return PMQA_ERR_NULL;
+  if (num_pages < 1 || num_requests < 1) return PMQA_ERR_SHAPE;
+  if (page_stride < (int64_t)PMQA_PAGE_TOKENS * head_dim * 2) return PMQA_ERR_SHAPE;
+  if (page_stride % 16 != 0) return PMQA_ERR_ALIGN;
+  if (bt_width < 1 || bt_stride < bt_width) return PMQA_ERR_SHAPE;
+  if ((int64_t)bt_width * PMQA_PAGE_TOKENS < max_context) return PMQA_ERR_SHAPE;
+  if (scores_row_stride < max_context) return PMQA_ERR_SHAPE;
+  if (!aligned16(query) || !aligned16(key_cache)) return PMQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(block_table) |
+       reinterpret_cast<uintptr_t>(context_lengths) | reinterpret_cast<uintptr_t>(requests) |
+       reinterpret_cast<uintptr_t>(group_row_offsets)) & 3)
+    return PMQA_ERR_ALIGN;
+  DeviceInfo* d = nullptr;
+  int rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
+  IdxArgs a;
+  a.q = static_cast<const uint16_t*>(query);
+  a.kc = static_cast<const uint8_t*>(key_cache);
+  a.page_stride = page_stride;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.lens = context_lengths;
+  a.reqs = requests;
+  a.offs = group_row_offsets;
+  a.scores = scores;
+  a.srs = scores_row_stride;
+  a.num_pages = num_pages;
+  a.num_requests = num_requests;
+  a.rows = rows;
+  a.groups = groups;
+  a.uniform_g = uniform_g;
+  a.max_context = max_context;
+  if (launch_indexer(a, static_cast<hipStream_t>(stream)) != hipSuccess) return PMQA_ERR_HIP;
+  return PMQA_OK;
+}
+
+int64_t mqa_logits_schedule_ints(int32_t num_units) {
+  if (num_units < 1 || num_units > (1 << 20)) return -1;
+  return kSchedHeader + 3 * ((int64_t)num_units + 1);
+}
+
+int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant) {
+  if (next_n < 1 || next_n > PMQA_MAX_NEXT_N) return PMQA_ERR_UNSUPPORTED;
+  if (variant != PMQA_VARIANT_FP8 && variant != PMQA_VARIANT_MXFP4) return PMQA_ERR_UNSUPPORTED;
+  int rc = init_device(device);
+  if (rc != PMQA_OK) return rc;
+  const DeviceInfo& d = g_dev[device];
+  const int out = variant == PMQA_VARIANT_FP8 ? 0 : 1;  // the variant's default output
+  return d.cus * d.occ[next_n - 1][variant][out] * (kBlockThreads / 64);
+}
+
+int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,
+                        int32_t max_context, int32_t num_units, int32_t* schedule,
+                        void* stream) {
+  if (batch < 0 || batch > PMQA_MAX_BATCH) return PMQA_ERR_SHAPE;
+  if (next_n < 1 || next_n > 64) return PMQA_ERR_SHAPE;
+  if (next_n > PMQA_MAX_NEXT_N) return PMQA_ERR_UNSUPPORTED;
+  if (variant != PMQA_VARIANT_FP8 && variant != PMQA_VARIANT_MXFP4) return PMQA_ERR_UNSUPPORTED;
+  if (max_context < 0 || max_context % PMQA_PAGE_TOKENS != 0) return PMQA_ERR_SHAPE;
+  if (num_units < 0 || num_units > (1 << 20)) return PMQA_ERR_SHAPE;
+  if (!schedule || (batch > 0 && !seq_lens)) return PMQA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(schedule) | reinterpret_cast<uintptr_t>(seq_lens)) & 3)
+    return PMQA_ERR_ALIGN;
+  if (num_units == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PMQA_ERR_HIP;
+    num_units = mqa_logits_num_units(dev, next_n, variant);
+    if (num_units < 0) return num_units;
+  } else {
+    DeviceInfo* d = nullptr;
+    int rc = current_device_info(&d);
+    if (rc != PMQA_OK) return rc;
+  }
+  if (launch_schedule(seq_lens, batch, next_n, variant, max_context, num_units, schedule,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PMQA_ERR_HIP;
+  return PMQA_OK;
+}
+
+int32_t mqa_logits_padded_seq_len(int32_t seq_len, int32_t next_n, int32_t variant) {
+  (void)next_n;
+  (void)variant;
+  if (seq_len <= 0) return 0;
+  return (int32_t)(((int64_t)seq_len + PMQA_PAGE_TOKENS - 1) / PMQA_PAGE_TOKENS *
+                   PMQA_PAGE_TOKENS);
+}
+
+int32_t mqa_logits_min_block_table_width(int32_t max_seq_len, int32_t next_n, int32_t variant) {
+  (void)next_n;
+  (void)variant;
+  if (max_seq_len <= 0) return 0;
+  return (int32_t)(((int64_t)max_seq_len + PMQA_PAGE_TOKENS - 1) / PMQA_PAGE_TOKENS);
+}
+
+int mqa_logits_init(int device) { return init_device(device); }
+
+const char* mqa_logits_status_string(int status) {
+  switch (status) {
+    case PMQA_OK: return "PMQA_OK";
+    case PMQA_ERR_NULL: return "PMQA_ERR_NULL: a required pointer is NULL";
+    case PMQA_ERR_SHAPE: return "PMQA_ERR_SHAPE: a size or stride is out of range";
+    case PMQA_ERR_UNSUPPORTED: return "PMQA_ERR_UNSUPPORTED: option not implemented";
+    case PMQA_ERR_ALIGN: return "PMQA_ERR_ALIGN: pointer or stride misaligned";
+    case PMQA_ERR_HIP: return "PMQA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown pmqa status";
+  }
+}
+
+}  // extern "C"

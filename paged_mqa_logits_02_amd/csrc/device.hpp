@@ -1,0 +1,110 @@
+// Device helpers for gfx950 (CDNA4): MFMA operand types, matrix-core
+// wrappers, cross-lane reductions and small load/store helpers.  Everything
+// here is wave64-specific.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmqa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kPage = 64;   // tokens per KV page
+constexpr int kWave = 64;   // lanes per wavefront
+constexpr int kE8M0One = 127;  // e8m0 code of 1.0
+
+constexpr int kFmtFp8 = 0;  // cbsz/blgp operand format: e4m3
+constexpr int kFmtFp4 = 4;  // cbsz/blgp operand format: e2m1
+
+// D[16x16] = A[16x128] * B[128x16] (+ C), e4m3 operands, fp32 accumulate.
+// Lane l holds row (l & 15) of A / column (l & 15) of B and 32 of the 128 K
+// values, in the same slots for A and B.  Output lane l, element i is
+// D[4*(l>>4) + i][l & 15].
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, kE8M0One,
+                                                          0, kE8M0One);
+}
+
+// Same shape with e2m1 operands (32 values = 16 bytes per lane) and one e8m0
+// block scale per lane and operand, applied to that lane's 32 values.
+__device__ __forceinline__ v4f mfma_fp4(const v4i& a, int sa, const v4i& b, int sb, const v4f& c) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, sa, 0,
+                                                          sb);
+}
+
+// D[16x16] = A[16x32] * B[32x16] (+ C), bf16 operands (8 per lane), fp32 accumulate.
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float relu(float x) { return __builtin_fmaxf(x, 0.0f); }
+
+// Sum of x over lanes l, l^32: v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+// v_permlane16_swap exchanges the odd 16-lane rows of the first operand with
+// the even rows of the second.
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Transposing reduction over the four 16-lane rows.  Input: four values a[s]
+// per lane.  Output (returned): in row g (lanes 16g..16g+15), lane l holds
+// sum over rows r of a[g] at lane 16r + (l & 15).
+__device__ __forceinline__ float row_transpose_reduce4(float a0, float a1, float a2, float a3) {
+  swap32(a0, a2);  // a0: rows 0,1 of old a0 | rows 0,1 of old a2 (upper half)
+  swap32(a1, a3);
+  float x = a0 + a2;  // rows 0-1: a0 halves summed; rows 2-3: a2 halves summed
+  float y = a1 + a3;  // rows 0-1: a1; rows 2-3: a3
+  swap16(x, y);
+  return x + y;  // row 0: a0, row 1: a1, row 2: a2, row 3: a3 (full sums)
+}
+
+// Sum over all four 16-lane rows, result in every row.
+__device__ __forceinline__ float row_reduce4(float a) {
+  float b = a;
+  swap32(a, b);
+  a += b;
+  b = a;
+  swap16(a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ T ldg_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+
+// Wave-wide inclusive prefix sum (64 lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+}  // namespace pmqa

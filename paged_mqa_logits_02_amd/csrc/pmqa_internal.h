@@ -1,0 +1,62 @@
+// Internal interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmqa {
+
+constexpr int kBlockThreads = 256;        // 4 wavefronts per workgroup
+constexpr int kSchedMagic = 0x41514D50;   // "PMQA"
+constexpr int kSchedHeader = 8;           // int32 header entries of a schedule
+constexpr int kMaxBatch = 8192;           // prefix of page counts kept in LDS
+
+// Arguments of the MQA logits kernels (FP8 and MXFP4).
+struct MqaArgs {
+  const uint8_t* q;        // fp8 [B,N,64,128] or packed fp4 [B,N,64,64]
+  const uint8_t* q_sf;     // e8m0 [B,N,64,4] (MXFP4 only)
+  const uint8_t* kv;       // pages
+  long long page_stride;   // bytes between pages
+  const float* w;          // [B*N, 64]
+  const int32_t* seq_lens; // [B]
+  const int32_t* bt;       // [B, bt_stride]
+  long long bt_stride;
+  void* out;               // [B*N, out_row_stride] f32 or bf16
+  long long out_row_stride;
+  const int32_t* schedule; // nullable
+  int num_pages;
+  int batch;
+  int max_context;
+  int pad_;
+};
+
+struct IdxArgs {
+  const uint16_t* q;        // bf16 [rows, 128]
+  const uint8_t* kc;        // pages of bf16 [64, 128]
+  long long page_stride;
+  const int32_t* bt;        // [num_requests, bt_stride]
+  long long bt_stride;
+  const int32_t* lens;      // [groups]
+  const int32_t* reqs;      // [groups]
+  const int32_t* offs;      // [groups+1] or null
+  float* scores;            // [rows, srs]
+  long long srs;
+  int num_pages;
+  int num_requests;
+  int rows;
+  int groups;
+  int uniform_g;            // rows per group when offs == null
+  int max_context;
+};
+
+const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype);
+const void* schedule_kernel_symbol();
+const void* indexer_kernel_symbol();
+
+hipError_t launch_mqa(const MqaArgs& a, int next_n, int variant, int out_dtype, int grid,
+                      size_t lds_bytes, hipStream_t stream);
+hipError_t launch_schedule(const int32_t* seq_lens, int B, int next_n, int variant,
+                           int max_context, int U, int32_t* sched, hipStream_t stream);
+hipError_t launch_indexer(const IdxArgs& a, hipStream_t stream);
+
+}  // namespace pmqa

@@ -1,0 +1,169 @@
+"""GPU-side helpers of the parity tests: move synthetic inputs to the device,
+call the library through its binding with sentinel-filled outputs, and compare
+with the oracle (written set exactly, values within the stated tolerance)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from fixtures_util import BF16_SENTINEL, F32_SENTINEL
+
+DEV = torch.device("cuda:0")
+
+# |gpu - ref| <= REL * A + ABS, A = s_p * sum_h |w| * relu(q.k)
+TOL_F32 = (2e-3, 1e-5)
+TOL_BF16 = (1e-2, 1e-5)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def pm():
+    import paged_mqa_logits_02_amd as m
+    return m
+
+
+class DevMqa:
+    """Device copies of a synth.MqaInputs."""
+
+    def __init__(self, inp, kv=None):
+        self.inp = inp
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        self.q = t(inp.q)
+        self.q_sf = t(inp.q_sf)
+        self.kv = t(inp.kv) if kv is None else kv
+        self.w = t(inp.weights)
+        self.sl = t(inp.seq_lens)
+        self.bt = t(inp.block_table)
+
+    def new_out(self, dtype=None):
+        inp = self.inp
+        if dtype is None:
+            dtype = torch.float32 if inp.out_dtype == "f32" else torch.bfloat16
+        out = torch.empty((inp.rows, inp.max_context), dtype=dtype, device=DEV)
+        if dtype == torch.float32:
+            out.view(torch.int32).fill_(F32_SENTINEL)
+        else:
+            out.view(torch.int16).fill_(BF16_SENTINEL)
+        return out
+
+    def run(self, out=None, schedule=None, dtype=None, stream=None):
+        if out is None:
+            out = self.new_out(dtype)
+        m = pm()
+        if self.inp.variant == "fp8":
+            m.mqa_logits_fp8(self.q, self.kv, self.w, self.sl, self.bt,
+                             max_context=self.inp.max_context, out=out, schedule_meta=schedule,
+                             stream=stream)
+        else:
+            m.mqa_logits_mxfp4(self.q, self.q_sf, self.kv, self.w, self.sl, self.bt,
+                               max_context=self.inp.max_context, out=out,
+                               schedule_meta=schedule, stream=stream)
+        return out
+
+
+def host_out(out):
+    """(values float64, written mask) of a device output buffer."""
+    torch.cuda.synchronize()
+    o = out.cpu()
+    if o.dtype == torch.float32:
+        bits = o.view(torch.int32).numpy().view(np.uint32)
+        wrote = bits != F32_SENTINEL
+        vals = o.numpy().astype(np.float64)
+    else:
+        bits = o.view(torch.int16).numpy().view(np.uint16)
+        wrote = bits != BF16_SENTINEL
+        vals = o.float().numpy().astype(np.float64)
+    return vals, wrote
+
+
+def tol_for(dtype):
+    return TOL_F32 if dtype == torch.float32 else TOL_BF16
+
+
+def check_values(got, ref, amag, tol, what=""):
+    rel, ab = tol
+    err = np.abs(got - ref)
+    lim = rel * amag + ab
+    bad = ~(err <= lim)
+    if bad.any():
+        i = np.argmax(np.where(bad, err / lim, 0))
+        raise AssertionError("%s: %d of %d values out of tolerance; worst got %r ref %r A %r" % (
+            what, int(bad.sum()), bad.size, got.flat[i], ref.flat[i], amag.flat[i]))
+    return float(np.max(err / lim)) if err.size else 0.0
+
+
+def check_dense(dm, out, what=""):
+    """Whole-output comparison against the dense oracle."""
+    got, wrote = host_out(out)
+    ref, amag, written = oracle.mqa_logits_for(dm.inp)
+    assert np.array_equal(wrote, written), "%s: written set differs (%d vs %d cells)" % (
+        what, int(wrote.sum()), int(written.sum()))
+    return check_values(got[written], ref[written], amag[written], tol_for(out.dtype), what)
+
+
+def sample_cells(inp, rng, per_request=24):
+    """Cells the oracle evaluates one by one at full size: per request the first
+    and last written columns, the meaningful limit of every slot and random
+    columns; plus random cells anywhere."""
+    rows, cols = [], []
+    N = inp.next_n
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        E = 0 if L <= 0 else min((L + 63) // 64 * 64, inp.max_context)
+        for t in range(N):
+            r = b * N + t
+            picks = [0, max(E - 1, 0), min(max(L - N + t, 0), inp.max_context - 1)]
+            picks += rng.integers(0, max(E, 1), per_request // N).tolist()
+            rows += [r] * len(picks)
+            cols += picks
+    n = 256
+    rows += rng.integers(0, inp.rows, n).tolist()
+    cols += rng.integers(0, inp.max_context, n).tolist()
+    return np.array(rows, np.int32), np.array(cols, np.int32)
+
+
+def check_sampled(dm, out, rng, what=""):
+    """Full-size comparison: the complete written set, values at sampled cells."""
+    inp = dm.inp
+    got, wrote = host_out(out)
+    written = oracle.mqa_written(inp.seq_lens, inp.batch, inp.next_n, inp.max_context)
+    assert np.array_equal(wrote, written), "%s: written set differs (%d vs %d cells)" % (
+        what, int(wrote.sum()), int(written.sum()))
+    rows, cols = sample_cells(inp, rng)
+    ref, amag, w = oracle.mqa_logits_points_for(inp, rows, cols)
+    assert np.array_equal(w, written[rows, cols])
+    return check_values(got[rows, cols][w], ref[w], amag[w], tol_for(out.dtype), what)
+
+
+class DevIndexer:
+    def __init__(self, ix, key_cache=None):
+        self.ix = ix
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+        self.q = t(ix.query.view(np.int16)).view(torch.bfloat16)
+        self.kc = t(ix.key_cache) if key_cache is None else key_cache
+        self.bt = t(ix.block_table)
+        self.lens = t(ix.context_lengths)
+        self.reqs = t(ix.requests)
+        self.offs = t(ix.group_row_offsets)
+
+    def run(self):
+        scores = torch.empty((self.ix.rows, self.ix.max_context), dtype=torch.float32, device=DEV)
+        scores.view(torch.int32).fill_(F32_SENTINEL)
+        pm().indexer_scores(self.q, self.kc, self.bt, self.lens, requests=self.reqs,
+                            scores=scores, group_row_offsets=self.offs)
+        return scores
+
+
+def check_indexer(di, scores, what=""):
+    got, wrote = host_out(scores)
+    ref, amag, written = oracle.indexer_scores_for(di.ix)
+    assert np.array_equal(wrote, written), "%s: written set differs (%d vs %d)" % (
+        what, int(wrote.sum()), int(written.sum()))
+    # one head: A = |q.k| (weight 1, no rectifier, no s_p)
+    return check_values(got[written], ref[written], np.abs(ref[written]), TOL_F32, what)

@@ -1,0 +1,139 @@
+"""The C-ABI library: it loads, exports every function include/pmqa.h declares,
+and its host-side validation returns the documented status codes.  None of
+these calls reaches the GPU (each is rejected, or is a no-op, before any
+launch), so they run without one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pmqa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, -1, -2, -3, -4
+FAKE = 0x10000  # an aligned, never dereferenced address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def pm():
+    from paged_mqa_logits_02_amd import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_mqa_logits_02_amd as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mqa_logits_fp8", "mqa_logits_mxfp4", "indexer_scores", "mqa_logits_schedule",
+              "mqa_logits_schedule_ints", "mqa_logits_num_units", "mqa_logits_padded_seq_len",
+              "mqa_logits_min_block_table_width", "mqa_logits_init", "mqa_logits_status_string"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(pm):
+    lib = ctypes.CDLL(pm.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_library_does_not_link_the_oracle(pm):
+    import subprocess
+    out = subprocess.run(["nm", "-D", pm.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+
+
+def test_helpers(pm):
+    assert pm.padded_seq_len(0) == 0 and pm.padded_seq_len(-4) == 0
+    assert pm.padded_seq_len(1) == 64 and pm.padded_seq_len(64) == 64
+    assert pm.padded_seq_len(65) == 128 and pm.padded_seq_len(32768) == 32768
+    assert pm.min_block_table_width(0) == 0 and pm.min_block_table_width(1) == 1
+    assert pm.min_block_table_width(200) == 4 and pm.min_block_table_width(131072) == 2048
+    assert pm.schedule_ints(1) == 8 + 3 * 2
+    assert pm.schedule_ints(0) == -1 and pm.schedule_ints(1 << 21) == -1
+    for s in (0, -1, -2, -3, -4, -6, 17):
+        assert isinstance(pm.status_string(s), str)
+
+
+def _fp8(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, ps=8448, npages=10, w=FAKE, sl=FAKE, bt=FAKE, bts=4, btw=4, B=2,
+             N=1, H=64, D=128, out=FAKE, ors=256, maxc=256, od=0, acc=0, sched=None,
+             stream=None)
+    a.update(kw)
+    return lib.mqa_logits_fp8(a["q"], a["kv"], a["ps"], a["npages"], a["w"], a["sl"], a["bt"],
+                              a["bts"], a["btw"], a["B"], a["N"], a["H"], a["D"], a["out"],
+                              a["ors"], a["maxc"], a["od"], a["acc"], a["sched"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(H=32), UNSUP), (dict(D=64), UNSUP), (dict(H=0), SHAPE), (dict(acc=1), UNSUP),
+    (dict(od=2), UNSUP), (dict(N=5), UNSUP), (dict(N=0), SHAPE), (dict(maxc=100), SHAPE),
+    (dict(maxc=-64), SHAPE), (dict(B=-1), SHAPE), (dict(B=8193), SHAPE),
+    (dict(q=None), NULL), (dict(kv=None), NULL), (dict(out=None), NULL), (dict(sl=None), NULL),
+    (dict(ps=8440), SHAPE), (dict(ps=8448 + 8), ALIGN), (dict(btw=3), SHAPE),
+    (dict(bts=3), SHAPE), (dict(ors=200), SHAPE), (dict(npages=0), SHAPE),
+    (dict(q=FAKE + 8), ALIGN), (dict(w=FAKE + 4), ALIGN), (dict(sl=FAKE + 2), ALIGN),
+    (dict(B=0), OK), (dict(maxc=0, ors=0), OK),
+])
+def test_fp8_validation(pm, kw, rc):
+    assert _fp8(pm.library(), **kw) == rc
+
+
+def _mx(lib, **kw):
+    a = dict(q=FAKE, qsf=FAKE, sfv=32, inter=0, kv=FAKE, ps=4352, npages=10, w=FAKE, sl=FAKE,
+             bt=FAKE, bts=4, btw=4, B=2, N=2, H=64, D=128, out=FAKE, ors=256, maxc=256, od=1,
+             sched=None, stream=None)
+    a.update(kw)
+    return lib.mqa_logits_mxfp4(a["q"], a["qsf"], a["sfv"], a["inter"], a["kv"], a["ps"],
+                                a["npages"], a["w"], a["sl"], a["bt"], a["bts"], a["btw"], a["B"],
+                                a["N"], a["H"], a["D"], a["out"], a["ors"], a["maxc"], a["od"],
+                                a["sched"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(sfv=16), UNSUP), (dict(inter=1), UNSUP), (dict(H=32), UNSUP), (dict(D=256), UNSUP),
+    (dict(qsf=None), NULL), (dict(ps=4340), SHAPE), (dict(ps=4352 + 4), ALIGN),
+    (dict(N=5), UNSUP), (dict(B=0), OK),
+])
+def test_mxfp4_validation(pm, kw, rc):
+    assert _mx(pm.library(), **kw) == rc
+
+
+def _idx(lib, **kw):
+    a = dict(q=FAKE, rows=24, D=128, kc=FAKE, ps=16384, npages=384, bt=FAKE, bts=64, btw=64,
+             nreq=6, lens=FAKE, reqs=FAKE, groups=6, offs=None, scores=FAKE, srs=4096,
+             maxc=4096, stream=None)
+    a.update(kw)
+    return lib.indexer_scores(a["q"], a["rows"], a["D"], a["kc"], a["ps"], a["npages"], a["bt"],
+                              a["bts"], a["btw"], a["nreq"], a["lens"], a["reqs"], a["groups"],
+                              a["offs"], a["scores"], a["srs"], a["maxc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(D=64), UNSUP), (dict(groups=5), SHAPE), (dict(groups=2), SHAPE),
+    (dict(groups=65536, rows=65536), SHAPE), (dict(maxc=4000), SHAPE),
+    (dict(ps=16384 - 16), SHAPE), (dict(ps=16384 + 8), ALIGN), (dict(btw=32), SHAPE),
+    (dict(srs=100), SHAPE), (dict(scores=None), NULL), (dict(reqs=None), NULL),
+    (dict(q=FAKE + 2), ALIGN), (dict(nreq=0), SHAPE), (dict(groups=0), OK),
+])
+def test_indexer_validation(pm, kw, rc):
+    assert _idx(pm.library(), **kw) == rc
+
+
+def test_schedule_validation(pm):
+    lib = pm.library()
+    assert lib.mqa_logits_schedule(FAKE, 4, 5, 0, 256, 8, FAKE, None) == UNSUP
+    assert lib.mqa_logits_schedule(FAKE, 4, 1, 2, 256, 8, FAKE, None) == UNSUP
+    assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 100, 8, FAKE, None) == SHAPE
+    assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 256, -1, FAKE, None) == SHAPE
+    assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 256, 8, None, None) == NULL
+    assert lib.mqa_logits_schedule(FAKE + 2, 4, 1, 0, 256, 8, FAKE, None) == ALIGN
+    assert lib.mqa_logits_num_units(0, 9, 0) == UNSUP

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Written sets are compared exactly (sentinel-filled outputs); values within
+|gpu - ref| <= 2e-3*A + 1e-5 (fp32 out) or 1e-2*A + 1e-5 (bf16 out), with
+A = s_p * sum_h |w| * relu(q.k); exact-arithmetic inputs bit-exactly."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fixtures_util import (extent, indexer_from_case, load_golden, mqa_from_case)
+from gpu_util import (DEV, DevIndexer, DevMqa, check_dense, check_indexer, check_sampled,
+                      host_out, pm, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    pm().init()
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------- small / exact
+
+
+def test_tiny_fp8_config():
+    inp = synth.make_config("tiny_fp8")
+    dm = DevMqa(inp)
+    say("tiny_fp8: B=2 N=1 seq_lens=%s" % inp.seq_lens.tolist())
+    r = check_dense(dm, dm.run(), "tiny_fp8")
+    say("tiny_fp8 max err/tol %.3g" % r)
+
+
+@pytest.mark.parametrize("case", load_golden("fp8_logits_cases.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_fp8_golden_bit_exact(case):
+    inp = mqa_from_case(case, "fp8")
+    got, wrote = host_out(DevMqa(inp).run())
+    E = extent(case["seq_len"], inp.max_context)
+    assert wrote[0, :E].all() and not wrote[0, E:].any()
+    for col, v in case["expected"].items():
+        assert got[0, int(col)] == v, (case["name"], col, got[0, int(col)])
+
+
+@pytest.mark.parametrize("case", load_golden("mxfp4_logits_cases.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_mxfp4_golden_bit_exact(case):
+    inp = mqa_from_case(case, "mxfp4")
+    for dtype in (torch.float32, torch.bfloat16):
+        got, _ = host_out(DevMqa(inp).run(dtype=dtype))
+        for col, v in case["expected"].items():
+            assert got[0, int(col)] == v, (case["name"], col, dtype)
+
+
+@pytest.mark.parametrize("case", load_golden("indexer_cases.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_indexer_golden_bit_exact(case):
+    di = DevIndexer(indexer_from_case(case))
+    got, wrote = host_out(di.run())
+    L = case["context_length"]
+    assert wrote[:, :L].all() and not wrote[:, L:].any()
+    for r, exp in enumerate(case["expected"]):
+        for col, v in exp.items():
+            if int(col) < L:
+                assert got[r, int(col)] == v
+
+
+RAGGED = [0, 1, 63, 64, 65, 200, 700, 1000, -5, 3000, 129, 2048]
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("next_n", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_batch(variant, next_n, dtype):
+    """Empty, one-token, page-boundary, negative and over-long (clamped)
+    lengths; every next_n; both output types."""
+    inp = synth.make_mqa_inputs(RAGGED, next_n, variant=variant, max_context=2048, bt_width=40,
+                                seed=100 + next_n, w_std=0.5, out_dtype=dtype, extra_pages=5)
+    say("ragged %s N=%d %s" % (variant, next_n, dtype))
+    dm = DevMqa(inp)
+    check_dense(dm, dm.run(), "ragged %s N=%d %s" % (variant, next_n, dtype))
+
+
+def _exact_inputs(variant, next_n, seed):
+    """Values on a coarse dyadic grid, so every partial sum is exact in fp32."""
+    rng = np.random.default_rng(seed)
+    inp = synth.make_mqa_inputs([300, 64, 1, 129], next_n, variant=variant, max_context=320,
+                                bt_width=5, seed=seed)
+    grid = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], dtype=np.float32)
+    qf = rng.choice(grid, (inp.batch, next_n, 64, 128)).astype(np.float32)
+    kf = rng.choice(grid, (inp.num_pages, 64, 128)).astype(np.float32)
+    if variant == "fp8":
+        inp.q = synth.encode_e4m3(qf)
+        inp.kv[:, : 64 * 128] = synth.encode_e4m3(kf).reshape(inp.num_pages, -1)
+        sp = np.ldexp(1.0, rng.integers(-4, 4, (inp.num_pages, 64))).astype(np.float32)
+        inp.kv[:, 64 * 128: 64 * 128 + 256] = sp.view(np.uint8)
+    else:
+        inp.q, inp.q_sf = synth.quantize_mxfp4(qf)
+        inp.q_sf[:] = 127
+        packed, _ = synth.quantize_mxfp4(kf)
+        inp.kv[:, : 64 * 64] = packed.reshape(inp.num_pages, -1)
+        inp.kv[:, 64 * 64: 64 * 64 + 256] = 127
+    inp.weights[:] = rng.choice(np.array([0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32),
+                                inp.weights.shape)
+    return inp
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("next_n", [1, 4])
+def test_exact_arithmetic_bit_exact(variant, next_n):
+    inp = _exact_inputs(variant, next_n, 200 + next_n)
+    ref, _, written = oracle.mqa_logits_for(inp)
+    dm = DevMqa(inp)
+    got, wrote = host_out(dm.run(dtype=torch.float32))
+    assert np.array_equal(wrote, written)
+    assert np.array_equal(got[written], ref[written])
+    gotb, _ = host_out(dm.run(dtype=torch.bfloat16))
+    refb = torch.from_numpy(ref[written]).float().bfloat16().double().numpy()
+    assert np.array_equal(gotb[written], refb)
+
+
+def test_one_head_fp8_equals_rectified_indexer_on_gpu():
+    rng = np.random.default_rng(20)
+    grid = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0])
+    inp = synth.make_mqa_inputs([100], 1, max_context=128, bt_width=2, seed=21)
+    qf = np.zeros((1, 1, 64, 128), dtype=np.float32)
+    qf[0, 0, 0] = rng.choice(grid, 128)
+    inp.q = synth.encode_e4m3(qf)
+    kf = rng.choice(grid, (inp.num_pages, 64, 128)).astype(np.float32)
+    inp.kv[:, : 64 * 128] = synth.encode_e4m3(kf).reshape(inp.num_pages, -1)
+    inp.kv[:, 64 * 128: 64 * 128 + 256] = np.ones((inp.num_pages, 64), np.float32).view(np.uint8)
+    inp.weights[:] = 0.0
+    inp.weights[0, 0] = 1.0
+    fp8, _ = host_out(DevMqa(inp).run())
+    kc = synth.encode_bf16(kf).view(np.uint8).reshape(inp.num_pages, -1)
+    ix = synth.IndexerInputs(synth.encode_bf16(qf[0, 0, :1]), kc, 64 * 128 * 2, inp.block_table,
+                             np.array([128], np.int32), np.array([0], np.int32),
+                             np.array([0, 1], np.int32), 128)
+    sc, _ = host_out(DevIndexer(ix).run())
+    assert np.array_equal(np.maximum(sc[0, :128], 0.0), fp8[0, :128])
+
+
+# ----------------------------------------------------------- indexer config
+
+
+@pytest.mark.parametrize("uniform", [None, 4, 1, 8])
+def test_indexer_config(uniform):
+    ix = synth.make_config("indexer_bf16", uniform_group=uniform)
+    say("indexer groups=%d uniform=%s lens=%s" % (ix.groups, uniform, ix.context_lengths.tolist()))
+    di = DevIndexer(ix)
+    check_indexer(di, di.run(), "indexer uniform=%s" % uniform)
+
+
+def test_indexer_strided_pages():
+    """Pages any multiple of 16 bytes apart: a view into a cache that holds
+    each page's keys and then other bytes."""
+    ix = synth.make_config("indexer_bf16")
+    wide = synth.make_config("indexer_bf16", page_stride=64 * 128 * 2 + 16 * 37)
+    a, _ = host_out(DevIndexer(ix).run())
+    b, _ = host_out(DevIndexer(wide).run())
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+# ------------------------------------------------------- full-size configs
+
+
+@pytest.mark.parametrize("name", ["decode_fp8", "verify_fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["in_call", "schedule"])
+def test_full_size_config(name, mode):
+    inp = synth.make_config(name)
+    say("%s %s: B=%d N=%d pages=%d positions=%d" % (name, mode, inp.batch, inp.next_n,
+                                                    inp.num_pages, inp.kv_positions()))
+    dm = DevMqa(inp)
+    sched = None
+    if mode == "schedule":
+        sched = pm().mqa_logits_schedule(dm.sl, inp.next_n,
+                                         0 if inp.variant == "fp8" else 1,
+                                         max_context=inp.max_context)
+    out = dm.run(schedule=sched)
+    r = check_sampled(dm, out, np.random.default_rng(7), "%s %s" % (name, mode))
+    say("%s %s max err/tol %.3g" % (name, mode, r))
+
+
+# ------------------------------------------------------- schedule / graphs
+
+
+def _mid_inputs(variant="fp8", next_n=2, seed=300):
+    lens = np.random.default_rng(seed).integers(0, 3000, 23)
+    lens[3] = 0
+    return synth.make_mqa_inputs(lens, next_n, variant=variant, max_context=3072, bt_width=48,
+                                 seed=seed)
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+def test_schedule_any_unit_count_bit_identical(variant):
+    inp = _mid_inputs(variant)
+    dm = DevMqa(inp)
+    base, wb = host_out(dm.run())
+    v = 0 if variant == "fp8" else 1
+    for U in (1, 7, 256, 1024, 5000, 0):
+        sched = pm().mqa_logits_schedule(dm.sl, inp.next_n, v, max_context=inp.max_context,
+                                         num_units=U)
+        got, wg = host_out(dm.run(schedule=sched))
+        assert np.array_equal(wb, wg), U
+        assert np.array_equal(got.view(np.uint64), base.view(np.uint64)), U
+    check_dense(dm, dm.run(), "mid %s" % variant)
+
+
+def test_schedule_for_other_arguments_is_ignored():
+    inp = _mid_inputs("fp8", next_n=2)
+    dm = DevMqa(inp)
+    base, _ = host_out(dm.run())
+    wrong = pm().mqa_logits_schedule(dm.sl, 3, 0, max_context=inp.max_context, num_units=64)
+    got, _ = host_out(dm.run(schedule=wrong))
+    assert np.array_equal(got.view(np.uint64), base.view(np.uint64))
+
+
+def test_repeat_runs_bit_identical():
+    inp = _mid_inputs("fp8", next_n=4, seed=301)
+    dm = DevMqa(inp)
+    a, _ = host_out(dm.run())
+    for _ in range(3):
+        b, _ = host_out(dm.run())
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def _graph_inputs(variant, seed):
+    """Same shapes for every seed: 23 requests, a full block table of
+    23 x 48 valid page ids, random lengths."""
+    lens = np.random.default_rng(seed).integers(0, 3000, 23)
+    lens[seed % 23] = 0
+    return synth.make_mqa_inputs(lens, 2, variant=variant, max_context=3072, bt_width=48,
+                                 seed=seed, full_table=True)
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+def test_graph_replay_with_changed_inputs(variant):
+    """Schedule + logits captured once; seq_lens, q, weights, pages and the
+    block table change between replays; every replay matches the oracle for
+    the inputs of that replay."""
+    inp = _graph_inputs(variant, 302)
+    dm = DevMqa(inp)
+    v = 0 if variant == "fp8" else 1
+    U = pm().num_units(inp.next_n, v)
+    sched = torch.empty(pm().schedule_ints(U), dtype=torch.int32, device=DEV)
+    out = dm.new_out()
+    dm.run(out=out)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pm().mqa_logits_schedule(dm.sl, inp.next_n, v, max_context=inp.max_context,
+                                 num_units=U, out=sched)
+        dm.run(out=out, schedule=sched)
+    for rep in range(3):
+        new = _graph_inputs(variant, 400 + rep)
+        dm.sl.copy_(torch.from_numpy(new.seq_lens))
+        dm.q.copy_(torch.from_numpy(new.q))
+        if new.q_sf is not None:
+            dm.q_sf.copy_(torch.from_numpy(new.q_sf))
+        dm.w.copy_(torch.from_numpy(new.weights))
+        dm.kv.copy_(torch.from_numpy(new.kv))
+        dm.bt.copy_(torch.from_numpy(new.block_table))
+        fresh = dm.new_out()
+        out.copy_(fresh)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        dm.inp = new
+        check_dense(dm, out, "%s replay %d" % (variant, rep))
+
+
+# ------------------------------------------------------------- invariants
+
+
+def test_strided_pages_identical():
+    a_in = _mid_inputs("fp8", next_n=1, seed=303)
+    b_in = synth.make_mqa_inputs(a_in.seq_lens, 1, max_context=3072, bt_width=48, seed=303,
+                                 page_stride=8448 + 16 * 5)
+    assert np.array_equal(a_in.kv, b_in.kv[:, :8448])
+    a, _ = host_out(DevMqa(a_in).run())
+    b, _ = host_out(DevMqa(b_in).run())
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_page_permutation_bit_exact():
+    inp = _mid_inputs("fp8", next_n=3, seed=304)
+    base, _ = host_out(DevMqa(inp).run())
+    perm = np.random.default_rng(1).permutation(inp.num_pages)
+    p2 = copy.copy(inp)
+    p2.kv = np.empty_like(inp.kv)
+    p2.kv[perm] = inp.kv
+    bt = inp.block_table.copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    p2.block_table = bt
+    got, _ = host_out(DevMqa(p2).run())
+    assert np.array_equal(got.view(np.uint64), base.view(np.uint64))
+
+
+def test_sp_power_of_two_scaling_exact():
+    inp = _mid_inputs("fp8", next_n=1, seed=305)
+    base, wrote = host_out(DevMqa(inp).run())
+    sc = copy.copy(inp)
+    sc.kv = inp.kv.copy()
+    s = sc.kv[:, 8192:8448].copy().view(np.float32) * np.float32(8.0)
+    sc.kv[:, 8192:8448] = s.view(np.uint8)
+    got, _ = host_out(DevMqa(sc).run())
+    assert np.array_equal(got[wrote], base[wrote] * 8.0)
+
+
+def test_poisoned_unread_data_never_reaches_outputs():
+    """Pages no request owns hold NaN codes (e4m3 0x7F, NaN scales); block-table
+    entries past each length are -1; zero-length requests have garbage rows."""
+    inp = synth.make_mqa_inputs([500, 0, 64, 1300], 2, max_context=1536, bt_width=24, seed=306,
+                                extra_pages=6)
+    used = set(inp.block_table[inp.block_table >= 0].tolist())
+    for p in range(inp.num_pages):
+        if p not in used:
+            inp.kv[p, :] = 0x7F
+            inp.kv[p, 8192:8448] = np.full(64, np.nan, np.float32).view(np.uint8)
+    dm = DevMqa(inp)
+    got, wrote = host_out(dm.run())
+    assert not np.isnan(got[wrote]).any()
+    check_dense(dm, dm.run(), "poisoned")
