@@ -28,10 +28,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def compile_flags():
-    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC]
+# Per-source extras.  The logits kernels: MFMA results in VGPRs (no copies out
+# of accumulation registers), and no NaN semantics for arithmetic so the
+# rectifier is one v_max_f32 (NaN outputs are written as bit patterns there).
+EXTRA_FLAGS = {"mqa_logits.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def compile_flags(src=None):
+    return (["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", INCLUDE, "-I", CSRC] + EXTRA_FLAGS.get(src, []))
 
 
 def build(verbose: bool = False) -> str:
@@ -41,7 +47,7 @@ def build(verbose: bool = False) -> str:
 
     def one(src):
         obj = os.path.join(BUILD_DIR, src + ".o")
-        cmd = [cc] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + compile_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

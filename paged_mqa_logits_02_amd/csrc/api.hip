@@ -14,6 +14,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceInfo {
   bool ready = false;
   int cus = 0;
+  size_t lds_per_cu = 0;
   // workgroups per CU for each kernel instance [next_n-1][variant][out]
   int occ[PMQA_MAX_NEXT_N][2][2] = {};
 };
@@ -35,14 +36,15 @@ int init_device(int device) {
     rc = PMQA_ERR_HIP;
   } else {
     d.cus = prop.multiProcessorCount;
+    d.lds_per_cu = prop.maxSharedMemoryPerMultiProcessor;
     for (int n = 1; n <= PMQA_MAX_NEXT_N && rc == PMQA_OK; ++n)
       for (int v = 0; v < 2 && rc == PMQA_OK; ++v)
         for (int o = 0; o < 2 && rc == PMQA_OK; ++o) {
           int blocks = 0;
-          // Occupancy with the LDS of a 4096-request batch; loads the code object.
+          // Occupancy from registers and the page ring; also loads the code object.
           if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                   &blocks, mqa_kernel_symbol(n, v, o), kBlockThreads,
-                  (4096 + 1) * sizeof(int)) != hipSuccess) {
+                  mqa_ring_bytes(v) + 64 * sizeof(int)) != hipSuccess) {
             rc = PMQA_ERR_HIP;
           }
           d.occ[n - 1][v][o] = blocks > 0 ? blocks : 1;
@@ -115,8 +117,15 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   a.batch = batch;
   a.max_context = max_context;
   a.pad_ = 0;
-  const int grid = d->cus * d->occ[next_n - 1][variant][out_dtype];
-  const size_t lds = (size_t)(batch + 1) * sizeof(int);
+  const size_t lds = mqa_ring_bytes(variant) + (size_t)(batch + 1) * sizeof(int);
+  int occ = d->occ[next_n - 1][variant][out_dtype];
+  if (d->lds_per_cu > 0) {
+    // whole 1 KiB allocation blocks plus the kernel's static LDS
+    const size_t per_block = (lds + 64 * sizeof(int) + 1023) / 1024 * 1024;
+    const int by_lds = (int)(d->lds_per_cu / per_block);
+    if (by_lds >= 1 && by_lds < occ) occ = by_lds;
+  }
+  const int grid = d->cus * occ;
   if (launch_mqa(a, next_n, variant, out_dtype, grid, lds, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return PMQA_ERR_HIP;

@@ -6,24 +6,37 @@
 // bullets after it; MXFP4 has no s_p and folds its block scales into q and k).
 //
 // Work decomposition.  The work items of a call are (request, 64-token page)
-// pairs in request-major order.  A wavefront is one "unit": it owns a
-// contiguous range of items, keeps the request's query (all 64 heads x N
-// slots) and head weights in registers, and streams the key pages of its range
-// straight from HBM into MFMA operand registers (a key token is used by one
-// wave only, so it never needs to be shared through LDS).  Ranges come either
-// from a schedule buffer or from an in-kernel split computed from seq_lens in
-// the prologue ("flashinfer.attn_scores", Scheduling and Setup: a per-call work
-// assignment computed on the GPU, so the call needs no host round-trip).
+// pairs in request-major order.  A workgroup (4 wavefronts) is one "unit": it
+// owns a contiguous range of items, taken either from a schedule buffer or
+// from an in-kernel split computed from seq_lens in the prologue
+// ("flashinfer.attn_scores", Scheduling and Setup: a per-call work assignment
+// computed on the GPU, so the call needs no host round-trip).
 //
-// Per page and wave: 4 token sub-tiles x 4 head tiles x N slots of
-// 16x16x128 MFMA; each lane then holds 4 heads x 1 token per tile.  The
-// rectifier and the weighted head sum run on those registers, one cross-row
-// transposing reduction leaves lane l with the logit of token l, which is
-// scaled by s_p and stored: 64 consecutive columns per row and page.
+// Data path per page.  The workgroup streams its pages through a ring of
+// kStages LDS slots with gfx950 direct-to-LDS loads (global_load_lds), so the
+// bytes in flight do not cost registers: kStages-1 pages are in flight while
+// one is scored.  The global side of each load is permuted so that the LDS
+// image is XOR-swizzled by row and the MFMA operand reads are free of bank
+// conflicts.  Each wave scores a share of the page (a subset of query slots
+// and 16-token sub-tiles) with its slice of the query and head weights held in
+// registers: 16x16x128 f8f6f4 MFMA (heads x tokens), rectifier and weighted
+// head sum in registers, a cross-row reduction with permlane swaps, s_p, and
+// a coalesced store of exactly the page's 64 columns.
 #include "device.hpp"
 #include "pmqa_internal.h"
 
+#ifndef PMQA_STAGES
+#define PMQA_STAGES 4
+#endif
+#ifdef PMQA_WAVES_PER_EU
+#define PMQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PMQA_WAVES_PER_EU)))
+#else
+#define PMQA_OCCUPANCY
+#endif
+
 namespace pmqa {
+
+constexpr int kStages = PMQA_STAGES;
 
 // --------------------------------------------------------------- schedule
 
@@ -73,7 +86,7 @@ __device__ __forceinline__ int locate(const int* s_prefix, int B, long long f) {
   int lo = 0, hi = B;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (s_prefix[mid] <= f) lo = mid; else hi = mid - 1;
+    if (__builtin_amdgcn_readfirstlane(s_prefix[mid]) <= f) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -107,29 +120,101 @@ __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict
   }
 }
 
+// ------------------------------------------------------- page staging (LDS)
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Lane i copies 16 (4) bytes from g to lds_base + 16i (4i); lds_base is uniform.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 4, 0, 0);
+}
+
+// Waits until at most N vector-memory loads of this wave are outstanding
+// (s_waitcnt vmcnt(N), other counters untouched).  The compiler's own waitcnt
+// tracking sees this wait; it does not track loads into LDS by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the page ring: waits for this wave's LDS reads only.
+// Neither __syncthreads() nor a workgroup fence can be used here: both make
+// the compiler wait for every load into LDS still in flight, which would drain
+// the ring.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Page layout per variant.  Key rows are stored in LDS with their 16-byte
+// chunks XOR-permuted by row (chunk c of row r sits in slot c ^ swz(r)), so
+// each group of 8 lanes of an MFMA operand read (128 bytes) touches all 32
+// banks once; rocprof's SQ_LDS_BANK_CONFLICT reads 0 with this layout.
+template <int VAR> struct PageLayout;
+
+template <> struct PageLayout<0> {       // FP8: 64 x 128 B keys, 64 fp32 scales
+  static constexpr int kRowBytes = 128;
+  static constexpr int kKeyBytes = kPage * kRowBytes;  // 8192
+  static constexpr int kStageBytes = kKeyBytes + kPage * 4;
+  static constexpr int kLoadsPerWave = 3;  // two 1 KB key chunks, one scale chunk
+  __device__ static int swz(int r) { return r & 7; }
+  // Wave w loads key rows 16w .. 16w+15 and scales of tokens 16w .. 16w+15.
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r0 = 8 * (2 * wave + i);
+      const int r = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      dma16(page + r * kRowBytes + c * 16, stage + r0 * kRowBytes);
+    }
+    if (lane < 16) dma4(page + kKeyBytes + 64 * wave + 4 * lane, stage + kKeyBytes + 64 * wave);
+  }
+};
+
+template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4 e8m0
+  static constexpr int kRowBytes = 64;
+  static constexpr int kKeyBytes = kPage * kRowBytes;  // 4096
+  static constexpr int kStageBytes = kKeyBytes + kPage * 4;
+  static constexpr int kLoadsPerWave = 2;
+  __device__ static int swz(int r) { return (r >> 1) & 3; }
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, int wave, int lane) {
+    const int r0 = 16 * wave;
+    const int r = r0 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    dma16(page + r * kRowBytes + c * 16, stage + r0 * kRowBytes);
+    if (lane < 16) dma4(page + kKeyBytes + 64 * wave + 4 * lane, stage + kKeyBytes + 64 * wave);
+  }
+};
+
 // ------------------------------------------------------------ operands
 
-// Per variant: the MFMA operand fragments of one 16-row tile and how they are
-// loaded.  The K dimension (head_dim) is split over lanes identically for the
-// query (A) and key (B) operand, so every product pairs matching d.
+// MFMA operand fragment of one 16-row tile.  The K dimension (head_dim) is
+// split over lanes identically for the query (A) and key (B) operand, so every
+// product pairs matching d.
 template <int VAR> struct Frag;
 
 // FP8: lane l holds d in [16g, 16g+16) and [64+16g, 64+16g+16), g = l>>4.
 template <> struct Frag<0> {
   v8i v;
-  static constexpr int kRowBytes = 128;  // head_dim e4m3
-  static constexpr int kKeyBytes = kPage * kRowBytes;
-  __device__ __forceinline__ void load(const uint8_t* row, int g) {
+  __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
     v4i lo = ldg<v4i>(row + 16 * g);
     v4i hi = ldg<v4i>(row + 64 + 16 * g);
     v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  __device__ __forceinline__ void load_stream(const uint8_t* row, int g) {
-    v4i lo = ldg_stream<v4i>(row + 16 * g);
-    v4i hi = ldg_stream<v4i>(row + 64 + 16 * g);
+  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
+    const int sw = PageLayout<0>::swz(r);
+    const uint8_t* row = stage + r * PageLayout<0>::kRowBytes;
+    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * (g ^ sw));
+    v4i hi = *reinterpret_cast<const v4i*>(row + 16 * ((4 + g) ^ sw));
     v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  __device__ __forceinline__ void zero() { v = (v8i){0, 0, 0, 0, 0, 0, 0, 0}; }
 };
 
 // MXFP4: lane l holds the 32-element block g = l>>4 (16 packed bytes) and that
@@ -137,15 +222,13 @@ template <> struct Frag<0> {
 template <> struct Frag<1> {
   v4i v;
   int sf;
-  static constexpr int kRowBytes = 64;  // 128 e2m1 values
-  static constexpr int kKeyBytes = kPage * kRowBytes;
-  __device__ __forceinline__ void load(const uint8_t* row, int g) { v = ldg<v4i>(row + 16 * g); }
-  __device__ __forceinline__ void load_stream(const uint8_t* row, int g) {
-    v = ldg_stream<v4i>(row + 16 * g);
+  __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
+    v = ldg<v4i>(row + 16 * g);
   }
-  __device__ __forceinline__ void zero() {
-    v = (v4i){0, 0, 0, 0};
-    sf = kE8M0One;
+  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
+    const int sw = PageLayout<1>::swz(r);
+    v = *reinterpret_cast<const v4i*>(stage + r * PageLayout<1>::kRowBytes + 16 * (g ^ sw));
+    sf = stage[PageLayout<1>::kKeyBytes + r * 4 + g];
   }
 };
 
@@ -156,197 +239,344 @@ __device__ __forceinline__ v4f mma(const Frag<1>& q, const Frag<1>& k) {
   return mfma_fp4(q.v, q.sf, k.v, k.sf, (v4f){0.f, 0.f, 0.f, 0.f});
 }
 
-// One page of keys for one wave: 4 sub-tiles of 16 tokens, plus the per-lane
-// FP8 scale of token l (MXFP4: 1).
-template <int VAR> struct PageFrag {
-  Frag<VAR> k[4];
-  float sp;
+// How the 4 waves of a workgroup share one page: each wave takes TW query
+// slots and SW 16-token sub-tiles.
+template <int N> struct WaveSplit;
+template <> struct WaveSplit<1> { static constexpr int TW = 1, SW = 1; };
+template <> struct WaveSplit<2> { static constexpr int TW = 1, SW = 2; };
+template <> struct WaveSplit<3> { static constexpr int TW = 3, SW = 1; };
+template <> struct WaveSplit<4> { static constexpr int TW = 1, SW = 4; };
+
+// The wave's query slots of request b (all 64 heads) and their head weights.
+template <int TW, int VAR> struct QueryFrag {
+  Frag<VAR> q[4][TW];  // [head tile][slot]
+  v4f w[4][TW];        // w[mt][t][i] = weight of head 16mt + 4(l>>4) + i
 };
 
-template <int VAR>
-__device__ __forceinline__ void load_page(PageFrag<VAR>& pf, const uint8_t* page, int lane) {
-  const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint8_t* row = page + (16 * s + r) * Frag<VAR>::kRowBytes;
-    pf.k[s].load_stream(row, g);
-  }
-  if constexpr (VAR == 0) {
-    pf.sp = ldg_stream<float>(page + Frag<0>::kKeyBytes + 4 * lane);
-  } else {
-    const uint8_t* sfp = page + Frag<1>::kKeyBytes;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf.k[s].sf = sfp[(16 * s + r) * 4 + g];
-    pf.sp = 1.0f;
-  }
+// Forces x to be complete in its registers here: the empty asm reads and
+// redefines it, so its load is waited for at this point and code after it
+// sees a plain register value (no pending load the compiler would wait on
+// inside the page loop, where that wait would drain the page ring).
+template <typename T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
-template <int VAR>
-__device__ __forceinline__ void zero_page(PageFrag<VAR>& pf) {
+template <int TW, int VAR>
+__device__ __forceinline__ void settle_query(QueryFrag<TW, VAR>& qf) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) pf.k[s].zero();
-  pf.sp = __builtin_nanf("");
-}
-
-// Query of request b (all heads, N slots) and its head weights.
-template <int N, int VAR> struct QueryFrag {
-  Frag<VAR> q[4][N];   // [head tile][slot]
-  v4f w[4][N];         // w[mt][t][i] = weight of head 16mt + 4(l>>4) + i
-};
-
-template <int N, int VAR>
-__device__ __forceinline__ void load_query(QueryFrag<N, VAR>& qf, const MqaArgs& a, int b,
-                                           int lane) {
-  const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-  for (int t = 0; t < N; ++t) {
+  for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const long long head_row = ((long long)(b * N + t) * 64 + 16 * mt + r);
-      qf.q[mt][t].load(a.q + head_row * Frag<VAR>::kRowBytes, g);
+      settle(qf.q[mt][t].v);
+      if constexpr (VAR == 1) settle(qf.q[mt][t].sf);
+      settle(qf.w[mt][t]);
+    }
+}
+
+template <int N, int TW, int VAR>
+__device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs& a, int b,
+                                           int t0, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  constexpr int kQRow = VAR == 0 ? 128 : 64;
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const long long head_row = ((long long)(b * N + t0 + t) * 64 + 16 * mt + r);
+      qf.q[mt][t].load_global(a.q + head_row * kQRow, g);
       if constexpr (VAR == 1) qf.q[mt][t].sf = a.q_sf[head_row * 4 + g];
-      qf.w[mt][t] = ldg<v4f>(a.w + (long long)(b * N + t) * 64 + 16 * mt + 4 * g);
+      qf.w[mt][t] = ldg<v4f>(a.w + (long long)(b * N + t0 + t) * 64 + 16 * mt + 4 * g);
     }
   }
 }
 
 // ------------------------------------------------------------- main kernel
 
+// Stores one logit; an output that depends on an out-of-range page id is a
+// quiet NaN, written as a bit pattern (this file is compiled without NaN
+// semantics for arithmetic, so no NaN is ever produced by arithmetic).
 template <int OUTT>
-__device__ __forceinline__ void store_logit(void* out, long long idx, float v) {
+__device__ __forceinline__ void store_logit(void* out, long long idx, float v, bool valid) {
   if constexpr (OUTT == 0) {
-    reinterpret_cast<float*>(out)[idx] = v;
+    const uint32_t bits = valid ? __float_as_uint(v) : 0x7FC00000u;
+    reinterpret_cast<uint32_t*>(out)[idx] = bits;
   } else {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
+    const uint16_t bits = valid ? f32_to_bf16_rne(v) : (uint16_t)0x7FC0u;
+    reinterpret_cast<uint16_t*>(out)[idx] = bits;
   }
 }
 
-// Scores one page for every slot and stores row b*N+t, columns 64j .. 64j+63.
+template <int VAR>
+__device__ __forceinline__ float stage_scale(const uint8_t* stage, int token) {
+  if constexpr (VAR == 0) {
+    return *reinterpret_cast<const float*>(stage + PageLayout<0>::kKeyBytes + 4 * token);
+  } else {
+    return 1.0f;
+  }
+}
+
+// Scores this wave's share of one staged page and stores it.
 template <int N, int VAR, int OUTT>
-__device__ __forceinline__ void score_page(const QueryFrag<N, VAR>& qf, const PageFrag<VAR>& pf,
-                                           const MqaArgs& a, int b, int j, int lane) {
-  float part[N][4];
+__device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR>& qf,
+                                           const uint8_t* stage, const MqaArgs& a, int b, int j,
+                                           bool valid, int t0, int s0, int lane) {
+  constexpr int TW = WaveSplit<N>::TW, SW = WaveSplit<N>::SW;
+  const int g = lane >> 4, rr = lane & 15;
+  float part[TW][SW];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int si = 0; si < SW; ++si) {
+    Frag<VAR> kf;
+    kf.load_stage(stage, 16 * (s0 + si) + rr, g);
+    // all matrix products of the sub-tile first, then the rectified head sums
+    v4f acc[TW][4];
 #pragma unroll
-    for (int t = 0; t < N; ++t) {
-      float sum = 0.0f;
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mma(qf.q[mt][t], kf);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      // two independent partial sums shorten the dependent FMA chain
+      float s_even = 0.0f, s_odd = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        v4f acc = mma(qf.q[mt][t], pf.k[s]);
         const v4f w = qf.w[mt][t];
-        sum = __builtin_fmaf(w[0], relu(acc[0]), sum);
-        sum = __builtin_fmaf(w[1], relu(acc[1]), sum);
-        sum = __builtin_fmaf(w[2], relu(acc[2]), sum);
-        sum = __builtin_fmaf(w[3], relu(acc[3]), sum);
+        s_even = __builtin_fmaf(w[0], relu(acc[t][mt][0]), s_even);
+        s_odd = __builtin_fmaf(w[1], relu(acc[t][mt][1]), s_odd);
+        s_even = __builtin_fmaf(w[2], relu(acc[t][mt][2]), s_even);
+        s_odd = __builtin_fmaf(w[3], relu(acc[t][mt][3]), s_odd);
       }
-      part[t][s] = sum;
+      part[t][si] = s_even + s_odd;
     }
+#ifdef PMQA_SUBTILE_FENCE
+    // keep each sub-tile's accumulators short-lived (fewer live registers)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
   }
+  const long long col0 = (long long)j * kPage;
+  if constexpr (SW == 4) {
+    // lane l ends with token l of the page
 #pragma unroll
-  for (int t = 0; t < N; ++t) {
-    float v = row_transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
-    if constexpr (VAR == 0) v *= pf.sp;
-    const long long idx = (long long)(b * N + t) * a.out_row_stride + (long long)j * kPage + lane;
-    store_logit<OUTT>(a.out, idx, v);
+    for (int t = 0; t < TW; ++t) {
+      float v = row_transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
+      v *= stage_scale<VAR>(stage, lane);
+      store_logit<OUTT>(a.out, (long long)(b * N + t0 + t) * a.out_row_stride + col0 + lane, v,
+                        valid);
+    }
+  } else if constexpr (SW == 2) {
+    // rows 0-1 end with sub-tile s0, rows 2-3 with s0+1
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      float x = part[t][0], y = part[t][1];
+      swap32(x, y);
+      float s = x + y;
+      float u = s;
+      swap16(s, u);
+      float v = s + u;
+      const int token = 16 * (s0 + (lane >> 5)) + rr;
+      v *= stage_scale<VAR>(stage, token);
+      if ((g & 1) == 0)
+        store_logit<OUTT>(a.out, (long long)(b * N + t0 + t) * a.out_row_stride + col0 + token, v,
+                          valid);
+    }
+  } else if constexpr (TW == 1) {
+    float v = row_reduce4(part[0][0]);
+    const int token = 16 * s0 + rr;
+    v *= stage_scale<VAR>(stage, token);
+    if (g == 0)
+      store_logit<OUTT>(a.out, (long long)(b * N + t0) * a.out_row_stride + col0 + token, v, valid);
+  } else {
+    static_assert(TW == 3 && SW == 1, "unsupported split");
+    // row g ends with slot g (rows 0..2)
+    float v = row_transpose_reduce4(part[0][0], part[1][0], part[2][0], 0.0f);
+    const int token = 16 * s0 + rr;
+    v *= stage_scale<VAR>(stage, token);
+    if (g < 3)
+      store_logit<OUTT>(a.out, (long long)(b * N + g) * a.out_row_stride + col0 + token, v, valid);
   }
 }
+
+// Values read from LDS are wave-uniform here; saying so keeps the cursors in
+// scalar registers and the page-id fetch a scalar load.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ int tiles_at(const int* s_prefix, int b) {
-  return s_prefix[b + 1] - s_prefix[b];
-}
-
-__device__ __forceinline__ void advance(const int* s_prefix, int B, int& b, int& j) {
-  ++j;
-  while (b < B && j >= tiles_at(s_prefix, b)) {
-    ++b;
-    j = 0;
-  }
-}
-
-__device__ __forceinline__ int page_id(const MqaArgs& a, int b, int j) {
-  return a.bt[(long long)b * a.bt_stride + j];
+  return uniform(s_prefix[b + 1] - s_prefix[b]);
 }
 
 __device__ __forceinline__ bool page_ok(const MqaArgs& a, int pg) {
   return (unsigned)pg < (unsigned)a.num_pages;
 }
 
-// Processes `count` items starting at (b, j).
-template <int N, int VAR, int OUTT>
-__device__ void process_range(const MqaArgs& a, const int* s_prefix, int b, int j, int count,
-                              int lane) {
-  const int B = a.batch;
-  while (b < B && j >= tiles_at(s_prefix, b)) { ++b; j = 0; }
-  if (count <= 0 || b >= B) return;
-
-  QueryFrag<N, VAR> qf;
-  load_query<N, VAR>(qf, a, b, lane);
-
-  PageFrag<VAR> cur, nxt;
-  int pg = page_id(a, b, j);
-  if (page_ok(a, pg)) load_page<VAR>(cur, a.kv + (long long)pg * a.page_stride, lane);
-  else zero_page<VAR>(cur);
-
-  int b1 = b, j1 = j;
-  advance(s_prefix, B, b1, j1);
-  int pg1 = (count > 1 && b1 < B) ? page_id(a, b1, j1) : -1;
-
-  for (int n = 0; n < count; ++n) {
-    const bool more = (n + 1 < count) && (b1 < B);
-    if (more) {
-      if (page_ok(a, pg1)) load_page<VAR>(nxt, a.kv + (long long)pg1 * a.page_stride, lane);
-      else zero_page<VAR>(nxt);
-    }
-    int b2 = b1, j2 = j1;
-    if (more) advance(s_prefix, B, b2, j2);
-    const int pg2 = (more && n + 2 < count && b2 < B) ? page_id(a, b2, j2) : -1;
-
-    score_page<N, VAR, OUTT>(qf, cur, a, b, j, lane);
-    if (!more) break;
-    if (b1 != b) load_query<N, VAR>(qf, a, b1, lane);
-    cur = nxt;
-    b = b1; j = j1;
-    b1 = b2; j1 = j2; pg1 = pg2;
+// Waits for the loads of the page scored now, given how many pages were
+// issued after it (0 .. kStages-2).
+template <int LPI>
+__device__ __forceinline__ void wait_page(int ahead) {
+  static_assert(kStages >= 2 && kStages <= 8, "stage count");
+  static_assert(6 * LPI < 64, "vmcnt range");
+  switch (ahead) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LPI>(); break;
+    case 2: wait_vmcnt<2 * LPI>(); break;
+    case 3: wait_vmcnt<3 * LPI>(); break;
+    case 4: wait_vmcnt<4 * LPI>(); break;
+    case 5: wait_vmcnt<5 * LPI>(); break;
+    default: wait_vmcnt<6 * LPI>(); break;
   }
 }
 
+constexpr int kPidTable = 512;  // page ids of the next items, in LDS
+
+// Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+511 (up
+// to f_end); entries past the end are not written.  Every thread maps its
+// item to (request, page) through the prefix in LDS.  Whole workgroup; the
+// caller places the barrier.
+__device__ __forceinline__ void fill_pid_table(const MqaArgs& a, const int* s_prefix, int* s_pid,
+                                               long long f, long long f_end) {
+  const long long P = uniform(s_prefix[a.batch]);
+  for (int t = threadIdx.x; t < kPidTable; t += blockDim.x) {
+    const long long fi = f + t;
+    if (fi < f_end) {
+      int pid = -1;
+      if (fi < P) {
+        int lo = 0, hi = a.batch;  // largest b with prefix[b] <= fi
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_prefix[mid] <= fi) lo = mid; else hi = mid - 1;
+        }
+        pid = a.bt[(long long)lo * a.bt_stride + (int)(fi - s_prefix[lo])];
+      }
+      s_pid[t] = pid;
+    }
+  }
+}
+
+// Scores flat items f0 .. f0+count-1, the whole workgroup together.
 template <int N, int VAR, int OUTT>
-__global__ void __launch_bounds__(256) mqa_logits_kernel(const MqaArgs a) {
-  extern __shared__ int s_prefix[];
+__device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid, uint8_t* ring,
+                              long long f0, int count) {
+  using L = PageLayout<VAR>;
+  constexpr int TW = WaveSplit<N>::TW, SW = WaveSplit<N>::SW, WS = 4 / SW;
+  const int B = a.batch;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int t0 = (wave / WS) * TW, s0 = (wave % WS) * SW;
+
+  const long long P = uniform(s_prefix[B]);
+  if (f0 < 0 || f0 >= P) return;
+  if (count > P - f0) count = (int)(P - f0);
+  if (count <= 0) return;
+  const long long f_end = f0 + count;
+  int b = locate(s_prefix, B, f0);
+  int j = (int)(f0 - uniform(s_prefix[b]));
+
+  fill_pid_table(a, s_prefix, s_pid, f0, f_end);
+  ring_barrier();
+
+  // Load side: runs kStages-1 items ahead of scoring.  A page id out of range
+  // is replaced by page 0 for the load (so every item issues the same loads)
+  // and its outputs are written as NaN.
+  int issued = 0;
+  uint32_t valid_bits = 0;  // bit (item % 32): page id was in range
+  auto issue_next = [&]() {
+    if (issued < count) {
+      if (issued % kPidTable == 0 && issued > 0) {
+        // next block of page ids; every wave gets here at the same item
+        ring_barrier();
+        fill_pid_table(a, s_prefix, s_pid, f0 + issued, f_end);
+        ring_barrier();
+      }
+      const int pid = uniform(s_pid[issued % kPidTable]);
+      const bool ok = page_ok(a, pid);
+      const uint8_t* page = a.kv + (long long)(ok ? pid : 0) * a.page_stride;
+      L::issue(ring + (issued % kStages) * L::kStageBytes, page, wave, lane);
+      valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
+      ++issued;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kStages - 1; ++k) issue_next();
+
+  int n = 0;
+  while (n < count && b < B) {
+    // One request: its query slice is loaded once.  It is the newest load,
+    // so waiting for it also waits for the pages in flight; this happens
+    // once per request.
+    QueryFrag<TW, VAR> qf;
+    load_query<N, TW, VAR>(qf, a, b, t0, lane);
+    settle_query(qf);
+    const int pages = min(count - n, tiles_at(s_prefix, b) - j);
+    for (int k = 0; k < pages; ++k, ++n, ++j) {
+      wait_page<L::kLoadsPerWave>(issued - n - 1);
+      ring_barrier();  // every wave's share of page n has landed; slot (n-1) is free
+      const bool valid = (valid_bits >> (n & 31)) & 1u;
+      issue_next();
+      score_page<N, VAR, OUTT>(qf, ring + (n % kStages) * L::kStageBytes, a, b, j, valid, t0,
+                               s0, lane);
+    }
+    // next request with pages
+    ++b;
+    j = 0;
+    while (b < B && tiles_at(s_prefix, b) == 0) ++b;
+  }
+  wait_vmcnt<0>();
+}
+
+template <int N, int VAR>
+constexpr int ring_bytes() {
+  return kStages * PageLayout<VAR>::kStageBytes;
+}
+
+// The tensor pointers are separate __restrict__ parameters so the compiler
+// knows the kernel's stores never alias its inputs and keeps wave-uniform
+// reads (block table, seq_lens, schedule) on the scalar cache.
+template <int N, int VAR, int OUTT>
+__global__ void __launch_bounds__(256) PMQA_OCCUPANCY
+    mqa_logits_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sf,
+                      const uint8_t* __restrict__ kv, const float* __restrict__ w,
+                      const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bt,
+                      const int32_t* __restrict__ schedule, void* __restrict__ out,
+                      const MqaArgs dims) {
+  MqaArgs a = dims;
+  a.q = q;
+  a.q_sf = q_sf;
+  a.kv = kv;
+  a.w = w;
+  a.seq_lens = seq_lens;
+  a.bt = bt;
+  a.schedule = schedule;
+  a.out = out;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_wsum[16];
+  __shared__ int s_pid[kPidTable];
+  uint8_t* ring = smem;
+  int* s_prefix = reinterpret_cast<int*>(smem + ring_bytes<N, VAR>());
   build_prefix(a.seq_lens, a.batch, a.max_context / kPage, s_prefix, s_wsum);
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int waves_per_block = blockDim.x / kWave;
   // Consecutive units on one XCD: workgroups are dealt to the 8 XCDs
   // round-robin, so renumber them XCD-major before splitting the work.
   const int G = gridDim.x;
-  const int blk = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int my_unit = blk * waves_per_block + wave;
-  const int total_waves = G * waves_per_block;
+  const int unit = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   const int32_t* sc = a.schedule;
   const bool use_sched = sc != nullptr && sc[0] == kSchedMagic && sc[2] == N &&
                          sc[3] == VAR && sc[4] == a.max_context && sc[5] == a.batch &&
                          sc[1] > 0;
   if (use_sched) {
+    // Units come from the schedule's split points (flat item indices); the
+    // request and page of each item are re-derived from the current seq_lens,
+    // so even a stale schedule cannot address outside the inputs.
     const int U = sc[1];
-    for (int u = my_unit; u < U; u += total_waves) {
+    for (int u = unit; u < U; u += G) {
       const int32_t* e = sc + kSchedHeader + 3 * u;
-      const int b = e[0], j = e[1];
-      const int count = e[5] - e[2];
-      if (b >= 0 && j >= 0) process_range<N, VAR, OUTT>(a, s_prefix, b, j, count, lane);
+      const long long f0 = e[2], f1 = e[5];
+      if (f1 > f0) process_range<N, VAR, OUTT>(a, s_prefix, s_pid, ring, f0, (int)(f1 - f0));
+      ring_barrier();  // the ring and the page-id table are reused by the next unit
     }
   } else {
-    const long long P = s_prefix[a.batch];
-    const long long f0 = (long long)my_unit * P / total_waves;
-    const long long f1 = (long long)(my_unit + 1) * P / total_waves;
-    if (f1 > f0) {
-      const int b = locate(s_prefix, a.batch, f0);
-      process_range<N, VAR, OUTT>(a, s_prefix, b, (int)(f0 - s_prefix[b]), (int)(f1 - f0), lane);
-    }
+    const long long P = uniform(s_prefix[a.batch]);
+    const long long f0 = (long long)unit * P / G;
+    const long long f1 = (long long)(unit + 1) * P / G;
+    if (f1 > f0) process_range<N, VAR, OUTT>(a, s_prefix, s_pid, ring, f0, (int)(f1 - f0));
   }
 }
 
@@ -358,10 +588,10 @@ static const void* kernel_ptr() {
 }
 
 const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype) {
-#define PMQA_K(n)                                                                  \
-  if (next_n == n) {                                                               \
+#define PMQA_K(n)                                                                         \
+  if (next_n == n) {                                                                      \
     if (variant == 0) return out_dtype == 0 ? kernel_ptr<n, 0, 0>() : kernel_ptr<n, 0, 1>(); \
-    return out_dtype == 0 ? kernel_ptr<n, 1, 0>() : kernel_ptr<n, 1, 1>();        \
+    return out_dtype == 0 ? kernel_ptr<n, 1, 0>() : kernel_ptr<n, 1, 1>();               \
   }
   PMQA_K(1)
   PMQA_K(2)
@@ -371,11 +601,23 @@ const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype) {
   return nullptr;
 }
 
+size_t mqa_ring_bytes(int variant) {
+  return variant == 0 ? (size_t)ring_bytes<1, 0>() : (size_t)ring_bytes<1, 1>();
+}
+
 hipError_t launch_mqa(const MqaArgs& a, int next_n, int variant, int out_dtype, int grid,
                       size_t lds_bytes, hipStream_t stream) {
   const void* fn = mqa_kernel_symbol(next_n, variant, out_dtype);
   if (!fn) return hipErrorInvalidValue;
-  void* args[] = {const_cast<MqaArgs*>(&a)};
+  const uint8_t* q = a.q;
+  const uint8_t* q_sf = a.q_sf;
+  const uint8_t* kv = a.kv;
+  const float* w = a.w;
+  const int32_t* seq_lens = a.seq_lens;
+  const int32_t* bt = a.bt;
+  const int32_t* sched = a.schedule;
+  void* out = a.out;
+  void* args[] = {&q, &q_sf, &kv, &w, &seq_lens, &bt, &sched, &out, const_cast<MqaArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(kBlockThreads), args, lds_bytes, stream);
 }
 

@@ -50,6 +50,7 @@ struct IdxArgs {
 };
 
 const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype);
+size_t mqa_ring_bytes(int variant);  // LDS of the page ring (before the request prefix)
 const void* schedule_kernel_symbol();
 const void* indexer_kernel_symbol();
 
