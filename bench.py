@@ -43,6 +43,44 @@ def algorithmic_bytes_per_position(variant, next_n, out_bytes):
     return 64 + 4 + next_n * out_bytes
 
 
+KERNEL_SOURCES = ["paged_mqa_logits_02_amd/csrc/mqa_logits.hip",
+                  "paged_mqa_logits_02_amd/csrc/device.hpp",
+                  "paged_mqa_logits_02_amd/csrc/pmqa_internal.h",
+                  "paged_mqa_logits_02_amd/build.py"]
+
+
+def kernel_source_hash():
+    """sha256 over the logits kernel's sources and build flags."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size); None if there is none or it was taken on
+    other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "mqa_logits_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, target_s=12.0):
     """The oracle (float64, as it stands) on a bounded sample of the same
     workload: random KV positions, every query slot of each."""
@@ -106,6 +144,8 @@ def main():
     ap.add_argument("--workload", default="verify_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="in_call", choices=["in_call", "schedule"])
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--ramp", type=float, default=1.0,
+                    help="seconds of untimed launches to bring the clock up before warmup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -165,7 +205,7 @@ def main():
 
     # Bring the engine clock up before the warmup steps (the first launches
     # after idle run at a lower clock); untimed.
-    t_ramp = time.time() + 1.0
+    t_ramp = time.time() + args.ramp
     i = 0
     while time.time() < t_ramp:
         step(i)
@@ -191,6 +231,7 @@ def main():
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_avg = float(np.mean(kern_ms))
 
+    traffic = counter_traffic(args.workload)
     positions = inp.kv_positions()
     bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes)
     alg_bytes = positions * bpp
@@ -220,10 +261,13 @@ def main():
             "schedule": args.mode, "kv_replicas": R, "units": U,
             "kernel_ms_avg": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
             "algorithmic_bytes_per_position": bpp,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "counter_bytes_per_launch": traffic,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
         },
     }
     if not args.no_cpu_baseline:
