@@ -428,35 +428,46 @@ __device__ __forceinline__ void wait_page(int ahead) {
 constexpr int kPidTable = 512;  // page ids of the next items, in LDS
 
 // Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+511 (up
-// to f_end); entries past the end are not written.  Every thread maps its
-// item to (request, page) through the prefix in LDS.  Whole workgroup; the
-// caller places the barrier.
+// to f_end); entries past the end are not written.  (b, j) is item f's
+// request and page.  Thread t walks from there to item f+t, request by
+// request (a unit spans few requests, so this is a few LDS reads).  Whole
+// workgroup; the caller places the barrier.
 __device__ __forceinline__ void fill_pid_table(const MqaArgs& a, const int* s_prefix, int* s_pid,
-                                               long long f, long long f_end) {
-  const long long P = uniform(s_prefix[a.batch]);
+                                               long long f, long long f_end, int b, int j) {
   for (int t = threadIdx.x; t < kPidTable; t += blockDim.x) {
-    const long long fi = f + t;
-    if (fi < f_end) {
-      int pid = -1;
-      if (fi < P) {
-        int lo = 0, hi = a.batch;  // largest b with prefix[b] <= fi
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_prefix[mid] <= fi) lo = mid; else hi = mid - 1;
-        }
-        pid = a.bt[(long long)lo * a.bt_stride + (int)(fi - s_prefix[lo])];
+    if (f + t < f_end) {
+      int bb = b, jj = j + t, pid = -1;
+      while (bb < a.batch) {
+        const int tiles = s_prefix[bb + 1] - s_prefix[bb];
+        if (jj < tiles) break;
+        jj -= tiles;
+        ++bb;
       }
+      if (bb < a.batch) pid = a.bt[(long long)bb * a.bt_stride + jj];
       s_pid[t] = pid;
     }
   }
 }
 
 // Scores flat items f0 .. f0+count-1, the whole workgroup together.
+//
+// Page pipeline.  Before waiting for page n, a wave issues its share of page
+// n + kAhead into the ring slot that page n + kAhead - kStages used:
+//  * when a wave scores only the 16-token sub-tile it loaded itself
+//    (next_n = 1 or 3), that slot is its own and was consumed in program
+//    order: no workgroup barrier at all, kAhead = kStages - 1;
+//  * otherwise (waves read sub-tiles other waves loaded) a barrier after
+//    page n has landed makes every share visible, and the slot issued into at
+//    iteration n belongs to page n - 2, which every wave finished before the
+//    barrier of iteration n - 1: kAhead = kStages - 2.
 template <int N, int VAR, int OUTT>
 __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid, uint8_t* ring,
                               long long f0, int count) {
   using L = PageLayout<VAR>;
   constexpr int TW = WaveSplit<N>::TW, SW = WaveSplit<N>::SW, WS = 4 / SW;
+  constexpr bool kShared = SW != 1;
+  constexpr int kAhead = kShared ? kStages - 2 : kStages - 1;
+  static_assert(kAhead >= 1, "ring too short");
   const int B = a.batch;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int t0 = (wave / WS) * TW, s0 = (wave % WS) * SW;
@@ -469,32 +480,37 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
   int b = locate(s_prefix, B, f0);
   int j = (int)(f0 - uniform(s_prefix[b]));
 
-  fill_pid_table(a, s_prefix, s_pid, f0, f_end);
+  fill_pid_table(a, s_prefix, s_pid, f0, f_end, b, j);
   ring_barrier();
 
-  // Load side: runs kStages-1 items ahead of scoring.  A page id out of range
-  // is replaced by page 0 for the load (so every item issues the same loads)
-  // and its outputs are written as NaN.
+  // A page id out of range is replaced by page 0 for the load (so every item
+  // issues the same loads) and its outputs are written as NaN.  The page id
+  // of the next item to issue is read one item ahead.
   int issued = 0;
   uint32_t valid_bits = 0;  // bit (item % 32): page id was in range
+  int pid_next = uniform(s_pid[0]);
   auto issue_next = [&]() {
     if (issued < count) {
-      if (issued % kPidTable == 0 && issued > 0) {
-        // next block of page ids; every wave gets here at the same item
-        ring_barrier();
-        fill_pid_table(a, s_prefix, s_pid, f0 + issued, f_end);
-        ring_barrier();
-      }
-      const int pid = uniform(s_pid[issued % kPidTable]);
-      const bool ok = page_ok(a, pid);
-      const uint8_t* page = a.kv + (long long)(ok ? pid : 0) * a.page_stride;
+      const bool ok = page_ok(a, pid_next);
+      const uint8_t* page = a.kv + (long long)(ok ? pid_next : 0) * a.page_stride;
       L::issue(ring + (issued % kStages) * L::kStageBytes, page, wave, lane);
       valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
       ++issued;
+      if (issued < count) {
+        if (issued % kPidTable == 0) {
+          // next block of page ids; every wave gets here at the same item
+          const long long f = f0 + issued;
+          const int rb = locate(s_prefix, B, f);
+          ring_barrier();
+          fill_pid_table(a, s_prefix, s_pid, f, f_end, rb, (int)(f - uniform(s_prefix[rb])));
+          ring_barrier();
+        }
+        pid_next = uniform(s_pid[issued % kPidTable]);
+      }
     }
   };
 #pragma unroll
-  for (int k = 0; k < kStages - 1; ++k) issue_next();
+  for (int k = 0; k < kAhead; ++k) issue_next();
 
   int n = 0;
   while (n < count && b < B) {
@@ -506,10 +522,10 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
     settle_query(qf);
     const int pages = min(count - n, tiles_at(s_prefix, b) - j);
     for (int k = 0; k < pages; ++k, ++n, ++j) {
-      wait_page<L::kLoadsPerWave>(issued - n - 1);
-      ring_barrier();  // every wave's share of page n has landed; slot (n-1) is free
-      const bool valid = (valid_bits >> (n & 31)) & 1u;
       issue_next();
+      wait_page<L::kLoadsPerWave>(issued - n - 1);
+      if constexpr (kShared) ring_barrier();  // every wave's share of page n has landed
+      const bool valid = (valid_bits >> (n & 31)) & 1u;
       score_page<N, VAR, OUTT>(qf, ring + (n % kStages) * L::kStageBytes, a, b, j, valid, t0,
                                s0, lane);
     }
