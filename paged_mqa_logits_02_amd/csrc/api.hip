@@ -15,9 +15,24 @@ struct DeviceInfo {
   bool ready = false;
   int cus = 0;
   size_t lds_per_cu = 0;
-  // workgroups per CU for each kernel instance [next_n-1][variant][out]
+  // workgroups per CU for each kernel instance [next_n-1][variant][out],
+  // from registers alone, and each instance's static LDS bytes
   int occ[PMQA_MAX_NEXT_N][2][2] = {};
+  size_t static_lds[PMQA_MAX_NEXT_N][2][2] = {};
 };
+
+// Resident workgroups per CU of a logits kernel instance launched with
+// `dyn_lds` bytes of dynamic LDS: the register limit, further limited by LDS
+// (dynamic plus static, in whole 1 KiB allocation blocks).
+int blocks_per_cu(const DeviceInfo& d, int next_n, int variant, int out, size_t dyn_lds) {
+  int occ = d.occ[next_n - 1][variant][out];
+  if (d.lds_per_cu > 0) {
+    const size_t per_block = (dyn_lds + d.static_lds[next_n - 1][variant][out] + 1023) / 1024 * 1024;
+    const int by_lds = (int)(d.lds_per_cu / per_block);
+    if (by_lds >= 1 && by_lds < occ) occ = by_lds;
+  }
+  return occ;
+}
 
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
@@ -41,13 +56,17 @@ int init_device(int device) {
       for (int v = 0; v < 2 && rc == PMQA_OK; ++v)
         for (int o = 0; o < 2 && rc == PMQA_OK; ++o) {
           int blocks = 0;
-          // Occupancy from registers and the page ring; also loads the code object.
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                  &blocks, mqa_kernel_symbol(n, v, o), kBlockThreads,
-                  mqa_ring_bytes(v) + 64 * sizeof(int)) != hipSuccess) {
+          hipFuncAttributes attr;
+          // Occupancy from registers (LDS is accounted per call, it depends
+          // on the batch); also loads the code object.
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mqa_kernel_symbol(n, v, o),
+                                                           kBlockThreads, 0) != hipSuccess ||
+              hipFuncGetAttributes(&attr, mqa_kernel_symbol(n, v, o)) != hipSuccess) {
             rc = PMQA_ERR_HIP;
+          } else {
+            d.occ[n - 1][v][o] = blocks > 0 ? blocks : 1;
+            d.static_lds[n - 1][v][o] = attr.sharedSizeBytes;
           }
-          d.occ[n - 1][v][o] = blocks > 0 ? blocks : 1;
         }
     hipFuncAttributes attr;
     if (rc == PMQA_OK && (hipFuncGetAttributes(&attr, schedule_kernel_symbol()) != hipSuccess ||
@@ -118,14 +137,7 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   a.max_context = max_context;
   a.pad_ = 0;
   const size_t lds = mqa_ring_bytes(variant) + (size_t)(batch + 1) * sizeof(int);
-  int occ = d->occ[next_n - 1][variant][out_dtype];
-  if (d->lds_per_cu > 0) {
-    // whole 1 KiB allocation blocks plus the kernel's static LDS
-    const size_t per_block = (lds + 64 * sizeof(int) + 1023) / 1024 * 1024;
-    const int by_lds = (int)(d->lds_per_cu / per_block);
-    if (by_lds >= 1 && by_lds < occ) occ = by_lds;
-  }
-  const int grid = d->cus * occ;
+  const int grid = d->cus * blocks_per_cu(*d, next_n, variant, out_dtype, lds);
   if (launch_mqa(a, next_n, variant, out_dtype, grid, lds, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return PMQA_ERR_HIP;
@@ -245,7 +257,8 @@ int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant) {
   if (rc != PMQA_OK) return rc;
   const DeviceInfo& d = g_dev[device];
   const int out = variant == PMQA_VARIANT_FP8 ? 0 : 1;  // the variant's default output
-  return d.cus * d.occ[next_n - 1][variant][out] * (kBlockThreads / 64);
+  const size_t lds = mqa_ring_bytes(variant) + sizeof(int);
+  return d.cus * blocks_per_cu(d, next_n, variant, out, lds) * (kBlockThreads / 64);
 }
 
 int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,

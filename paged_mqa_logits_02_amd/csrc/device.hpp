@@ -11,6 +11,7 @@ namespace pmqa {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kPage = 64;   // tokens per KV page
@@ -36,6 +37,25 @@ __device__ __forceinline__ v4f mfma_fp4(const v4i& a, int sa, const v4i& b, int 
   v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, sa, 0,
                                                           sb);
+}
+
+// D[32x32] = A[32x64] * B[64x32] (+ C), e4m3 operands, fp32 accumulate.
+// Lane l holds row (l & 31) of A / column (l & 31) of B and 32 of the 64 K
+// values, in the same slots for A and B.  Output lane l, element i is
+// D[8*(i>>2) + 4*(l>>5) + (i&3)][l & 31].
+__device__ __forceinline__ v16f mfma32_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, kE8M0One,
+                                                         0, kE8M0One);
+}
+
+// Same shape with e2m1 operands (32 values = 16 bytes per lane) and one e8m0
+// block scale per lane and operand.
+__device__ __forceinline__ v16f mfma32_fp4(const v4i& a, int sa, const v4i& b, int sb,
+                                           const v16f& c) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, sa, 0,
+                                                         sb);
 }
 
 // D[16x16] = A[16x32] * B[32x16] (+ C), bf16 operands (8 per lane), fp32 accumulate.

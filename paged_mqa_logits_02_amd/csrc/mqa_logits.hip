@@ -154,9 +154,10 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // Page layout per variant.  Key rows are stored in LDS with their 16-byte
-// chunks XOR-permuted by row (chunk c of row r sits in slot c ^ swz(r)), so
-// each group of 8 lanes of an MFMA operand read (128 bytes) touches all 32
-// banks once; rocprof's SQ_LDS_BANK_CONFLICT reads 0 with this layout.
+// chunks XOR-permuted by row (chunk c of row r sits in slot c ^ swz(r)).  The
+// permutations were chosen by measurement (rocprof SQ_LDS_BANK_CONFLICT = 0)
+// for both operand read patterns: 16 consecutive rows per 16 lanes (16x16
+// tiles) and 32 consecutive rows per 32 lanes (32x32 tiles).
 template <int VAR> struct PageLayout;
 
 template <> struct PageLayout<0> {       // FP8: 64 x 128 B keys, 64 fp32 scales
@@ -164,17 +165,30 @@ template <> struct PageLayout<0> {       // FP8: 64 x 128 B keys, 64 fp32 scales
   static constexpr int kKeyBytes = kPage * kRowBytes;  // 8192
   static constexpr int kStageBytes = kKeyBytes + kPage * 4;
   static constexpr int kLoadsPerWave = 3;  // two 1 KB key chunks, one scale chunk
-  __device__ static int swz(int r) { return r & 7; }
+  __device__ static int swz(int r) { return (r >> 1) & 7; }
   // Wave w loads key rows 16w .. 16w+15 and scales of tokens 16w .. 16w+15.
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, int wave, int lane) {
+  // The per-lane byte offsets inside a page do not change from page to page;
+  // they are computed once, so a page's loads take a uniform base address and
+  // these offsets (no per-page vector arithmetic).
+  struct Lanes {
+    uint32_t key[2];
+    uint32_t scale;
+  };
+  __device__ static Lanes lanes(int wave, int lane) {
+    Lanes o;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r0 = 8 * (2 * wave + i);
-      const int r = r0 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      dma16(page + r * kRowBytes + c * 16, stage + r0 * kRowBytes);
+      const int r = 8 * (2 * wave + i) + (lane >> 3);
+      o.key[i] = r * kRowBytes + 16 * ((lane & 7) ^ swz(r));
     }
-    if (lane < 16) dma4(page + kKeyBytes + 64 * wave + 4 * lane, stage + kKeyBytes + 64 * wave);
+    o.scale = kKeyBytes + 64 * wave + 4 * (lane & 15);
+    return o;
+  }
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
+                               int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(page + o.key[i], stage + 8 * (2 * wave + i) * kRowBytes);
+    if (lane < 16) dma4(page + o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 
@@ -184,12 +198,21 @@ template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4
   static constexpr int kStageBytes = kKeyBytes + kPage * 4;
   static constexpr int kLoadsPerWave = 2;
   __device__ static int swz(int r) { return (r >> 1) & 3; }
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, int wave, int lane) {
-    const int r0 = 16 * wave;
-    const int r = r0 + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
-    dma16(page + r * kRowBytes + c * 16, stage + r0 * kRowBytes);
-    if (lane < 16) dma4(page + kKeyBytes + 64 * wave + 4 * lane, stage + kKeyBytes + 64 * wave);
+  struct Lanes {
+    uint32_t key;
+    uint32_t scale;
+  };
+  __device__ static Lanes lanes(int wave, int lane) {
+    const int r = 16 * wave + (lane >> 2);
+    Lanes o;
+    o.key = r * kRowBytes + 16 * ((lane & 3) ^ swz(r));
+    o.scale = kKeyBytes + 64 * wave + 4 * (lane & 15);
+    return o;
+  }
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
+                               int lane) {
+    dma16(page + o.key, stage + 16 * wave * kRowBytes);
+    if (lane < 16) dma4(page + o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 
@@ -240,12 +263,63 @@ __device__ __forceinline__ v4f mma(const Frag<1>& q, const Frag<1>& k) {
 }
 
 // How the 4 waves of a workgroup share one page: each wave takes TW query
-// slots and SW 16-token sub-tiles.
+// slots and SW 16-token sub-tiles.  kWide: the wave's share is scored with
+// 32x32x64 MFMA tiles (32 heads x 32 tokens) instead of 16x16x128 ones; half
+// the matrix instructions for the same products, and a lane then holds 16
+// heads of one token, so the head reduction is a single cross-half exchange.
 template <int N> struct WaveSplit;
-template <> struct WaveSplit<1> { static constexpr int TW = 1, SW = 1; };
-template <> struct WaveSplit<2> { static constexpr int TW = 1, SW = 2; };
-template <> struct WaveSplit<3> { static constexpr int TW = 3, SW = 1; };
-template <> struct WaveSplit<4> { static constexpr int TW = 1, SW = 4; };
+template <> struct WaveSplit<1> { static constexpr int TW = 1, SW = 1; static constexpr bool kWide = false; };
+template <> struct WaveSplit<2> { static constexpr int TW = 1, SW = 2; static constexpr bool kWide = false; };
+template <> struct WaveSplit<3> { static constexpr int TW = 3, SW = 1; static constexpr bool kWide = false; };
+template <> struct WaveSplit<4> { static constexpr int TW = 1, SW = 4; static constexpr bool kWide = true; };
+
+// 32x32x64 operand fragment of one K step (64 of the 128 head_dim values):
+// lane l holds row (l & 31) and K values [32h, 32h + 32) of the step,
+// h = l >> 5, in the same slots for the query and the key operand.
+template <int VAR> struct WideFrag;
+
+// FP8: step ks covers bytes [64ks, 64ks + 64) of a row; 32 bytes per lane.
+template <> struct WideFrag<0> {
+  v8i v;
+  __device__ __forceinline__ void load_global(const uint8_t* row, int ks, int h) {
+    v4i lo = ldg<v4i>(row + 64 * ks + 32 * h);
+    v4i hi = ldg<v4i>(row + 64 * ks + 32 * h + 16);
+    v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
+    const int sw = PageLayout<0>::swz(r);
+    const int c = 4 * ks + 2 * h;
+    const uint8_t* row = stage + r * PageLayout<0>::kRowBytes;
+    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * (c ^ sw));
+    v4i hi = *reinterpret_cast<const v4i*>(row + 16 * ((c + 1) ^ sw));
+    v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// MXFP4: lane l holds 32-element block 2ks + h of the row (16 packed bytes)
+// and that block's e8m0 code.
+template <> struct WideFrag<1> {
+  v4i v;
+  int sf;
+  __device__ __forceinline__ void load_global(const uint8_t* row, int ks, int h) {
+    v = ldg<v4i>(row + 16 * (2 * ks + h));
+  }
+  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
+    const int c = 2 * ks + h;
+    v = *reinterpret_cast<const v4i*>(stage + r * PageLayout<1>::kRowBytes +
+                                      16 * (c ^ PageLayout<1>::swz(r)));
+    sf = stage[PageLayout<1>::kKeyBytes + r * 4 + c];
+  }
+};
+
+__device__ __forceinline__ v16f mma_wide(const WideFrag<0>& q, const WideFrag<0>& k,
+                                         const v16f& c) {
+  return mfma32_fp8(q.v, k.v, c);
+}
+__device__ __forceinline__ v16f mma_wide(const WideFrag<1>& q, const WideFrag<1>& k,
+                                         const v16f& c) {
+  return mfma32_fp4(q.v, q.sf, k.v, k.sf, c);
+}
 
 // The wave's query slots of request b (all 64 heads) and their head weights.
 template <int TW, int VAR> struct QueryFrag {
@@ -288,6 +362,47 @@ __device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs
       if constexpr (VAR == 1) qf.q[mt][t].sf = a.q_sf[head_row * 4 + g];
       qf.w[mt][t] = ldg<v4f>(a.w + (long long)(b * N + t0 + t) * 64 + 16 * mt + 4 * g);
     }
+  }
+}
+
+// The wave's one query slot of request b for 32x32 tiles: q[mt][ks] covers
+// heads 32mt + (l & 31), K step ks; w[mt][u][i] is the weight of head
+// 32mt + 8u + 4(l >> 5) + i, the head of output element 4u + i of tile mt.
+template <int VAR> struct WideQuery {
+  WideFrag<VAR> q[2][2];
+  v4f w[2][4];
+};
+
+template <int VAR>
+__device__ __forceinline__ void settle_query(WideQuery<VAR>& qf) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      settle(qf.q[mt][ks].v);
+      if constexpr (VAR == 1) settle(qf.q[mt][ks].sf);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) settle(qf.w[mt][u]);
+  }
+}
+
+template <int N, int VAR>
+__device__ __forceinline__ void load_query(WideQuery<VAR>& qf, const MqaArgs& a, int b, int t0,
+                                           int lane) {
+  const int h = lane >> 5, r = lane & 31;
+  constexpr int kQRow = VAR == 0 ? 128 : 64;
+  const long long slot = (long long)b * N + t0;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const long long head_row = slot * 64 + 32 * mt + r;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qf.q[mt][ks].load_global(a.q + head_row * kQRow, ks, h);
+      if constexpr (VAR == 1) qf.q[mt][ks].sf = a.q_sf[head_row * 4 + 2 * ks + h];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qf.w[mt][u] = ldg<v4f>(a.w + slot * 64 + 32 * mt + 8 * u + 4 * h);
   }
 }
 
@@ -386,14 +501,62 @@ __device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR
     if (g == 0)
       store_logit<OUTT>(a.out, (long long)(b * N + t0) * a.out_row_stride + col0 + token, v, valid);
   } else {
-    static_assert(TW == 3 && SW == 1, "unsupported split");
-    // row g ends with slot g (rows 0..2)
-    float v = row_transpose_reduce4(part[0][0], part[1][0], part[2][0], 0.0f);
+    static_assert((TW == 3 || TW == 4) && SW == 1, "unsupported split");
+    // row g ends with slot g
+    float v = row_transpose_reduce4(part[0][0], part[1][0], part[2][0],
+                                    TW == 4 ? part[TW - 1][0] : 0.0f);
     const int token = 16 * s0 + rr;
     v *= stage_scale<VAR>(stage, token);
-    if (g < 3)
+    if (g < TW)
       store_logit<OUTT>(a.out, (long long)(b * N + g) * a.out_row_stride + col0 + token, v, valid);
   }
+}
+
+// Scores this wave's share of one staged page with 32x32 tiles: one query
+// slot, SW/2 32-token halves starting at half s0/2.  All key fragments of the
+// share are read from LDS first so their latency overlaps the first products.
+template <int N, int VAR, int OUTT>
+__device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8_t* stage,
+                                           const MqaArgs& a, int b, int j, bool valid, int t0,
+                                           int s0, int lane) {
+  constexpr int NT = WaveSplit<N>::SW / 2;
+  static_assert(NT == 1 || NT == 2, "wide split covers one or two halves");
+  const int h = lane >> 5, rr = lane & 31, nt0 = s0 / 2;
+  WideFrag<VAR> kf[NT][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) kf[nt][ks].load_stage(stage, 32 * (nt0 + nt) + rr, ks, h);
+  const int token = NT == 2 ? lane : 32 * nt0 + rr;
+  const float sp = stage_scale<VAR>(stage, token);
+  float part[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    // the two head tiles alternate so that no product waits on the one just issued
+    v16f acc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.q[mt][0], kf[nt][0], (v16f){});
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.q[mt][1], kf[nt][1], acc[mt]);
+    float s_even = 0.0f, s_odd = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v4f w = qf.w[mt][u];
+        s_even = __builtin_fmaf(w[0], relu(acc[mt][4 * u + 0]), s_even);
+        s_odd = __builtin_fmaf(w[1], relu(acc[mt][4 * u + 1]), s_odd);
+        s_even = __builtin_fmaf(w[2], relu(acc[mt][4 * u + 2]), s_even);
+        s_odd = __builtin_fmaf(w[3], relu(acc[mt][4 * u + 3]), s_odd);
+      }
+    part[nt] = s_even + s_odd;
+  }
+  // lanes l and l ^ 32 hold the two head halves of one token
+  float x = part[0], y = part[NT - 1];
+  swap32(x, y);
+  const float v = (x + y) * sp;  // NT == 2: lane l has token l; else lanes < 32 have it
+  const long long idx = (long long)(b * N + t0) * a.out_row_stride + (long long)j * kPage + token;
+  if (NT == 2 || h == 0) store_logit<OUTT>(a.out, idx, v, valid);
 }
 
 // Values read from LDS are wave-uniform here; saying so keeps the cursors in
@@ -409,20 +572,28 @@ __device__ __forceinline__ bool page_ok(const MqaArgs& a, int pg) {
 }
 
 // Waits for the loads of the page scored now, given how many pages were
-// issued after it (0 .. kStages-2).
-template <int LPI>
+// issued after it (`ahead`, 0 .. kMax).  The steady state (kMax pages ahead)
+// is tested first; fewer pages are ahead only at the end of a range.
+template <int LPI, int kMax>
 __device__ __forceinline__ void wait_page(int ahead) {
-  static_assert(kStages >= 2 && kStages <= 8, "stage count");
-  static_assert(6 * LPI < 64, "vmcnt range");
-  switch (ahead) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<LPI>(); break;
-    case 2: wait_vmcnt<2 * LPI>(); break;
-    case 3: wait_vmcnt<3 * LPI>(); break;
-    case 4: wait_vmcnt<4 * LPI>(); break;
-    case 5: wait_vmcnt<5 * LPI>(); break;
-    default: wait_vmcnt<6 * LPI>(); break;
+  static_assert(kMax * LPI < 64, "vmcnt range");
+  if (ahead >= kMax) {
+    wait_vmcnt<kMax * LPI>();
+  } else if constexpr (kMax > 1) {
+    wait_page<LPI, kMax - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
   }
+}
+
+template <bool Wide, int N, int VAR> struct QueryPick { using type = QueryFrag<WaveSplit<N>::TW, VAR>; };
+template <int N, int VAR> struct QueryPick<true, N, VAR> { using type = WideQuery<VAR>; };
+template <int N, int VAR> struct QueryOf : QueryPick<WaveSplit<N>::kWide, N, VAR> {};
+
+template <int N, int VAR, typename Q>
+__device__ __forceinline__ void load_query_any(Q& qf, const MqaArgs& a, int b, int t0, int lane) {
+  if constexpr (WaveSplit<N>::kWide) load_query<N, VAR>(qf, a, b, t0, lane);
+  else load_query<N, WaveSplit<N>::TW, VAR>(qf, a, b, t0, lane);
 }
 
 constexpr int kPidTable = 512;  // page ids of the next items, in LDS
@@ -469,8 +640,9 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
   constexpr int kAhead = kShared ? kStages - 2 : kStages - 1;
   static_assert(kAhead >= 1, "ring too short");
   const int B = a.batch;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int t0 = (wave / WS) * TW, s0 = (wave % WS) * SW;
+  const typename L::Lanes dma_lanes = L::lanes(wave, lane);
 
   const long long P = uniform(s_prefix[B]);
   if (f0 < 0 || f0 >= P) return;
@@ -493,7 +665,7 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
     if (issued < count) {
       const bool ok = page_ok(a, pid_next);
       const uint8_t* page = a.kv + (long long)(ok ? pid_next : 0) * a.page_stride;
-      L::issue(ring + (issued % kStages) * L::kStageBytes, page, wave, lane);
+      L::issue(ring + ((unsigned)issued % kStages) * L::kStageBytes, page, dma_lanes, wave, lane);
       valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
       ++issued;
       if (issued < count) {
@@ -517,16 +689,16 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
     // One request: its query slice is loaded once.  It is the newest load,
     // so waiting for it also waits for the pages in flight; this happens
     // once per request.
-    QueryFrag<TW, VAR> qf;
-    load_query<N, TW, VAR>(qf, a, b, t0, lane);
+    typename QueryOf<N, VAR>::type qf;
+    load_query_any<N, VAR>(qf, a, b, t0, lane);
     settle_query(qf);
     const int pages = min(count - n, tiles_at(s_prefix, b) - j);
     for (int k = 0; k < pages; ++k, ++n, ++j) {
       issue_next();
-      wait_page<L::kLoadsPerWave>(issued - n - 1);
+      wait_page<L::kLoadsPerWave, kAhead>(issued - n - 1);
       if constexpr (kShared) ring_barrier();  // every wave's share of page n has landed
       const bool valid = (valid_bits >> (n & 31)) & 1u;
-      score_page<N, VAR, OUTT>(qf, ring + (n % kStages) * L::kStageBytes, a, b, j, valid, t0,
+      score_page<N, VAR, OUTT>(qf, ring + ((unsigned)n % kStages) * L::kStageBytes, a, b, j, valid, t0,
                                s0, lane);
     }
     // next request with pages
