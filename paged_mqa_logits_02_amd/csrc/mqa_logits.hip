@@ -269,7 +269,7 @@ __device__ __forceinline__ v4f mma(const Frag<1>& q, const Frag<1>& k) {
 // heads of one token, so the head reduction is a single cross-half exchange.
 template <int N> struct WaveSplit;
 template <> struct WaveSplit<1> { static constexpr int TW = 1, SW = 1; static constexpr bool kWide = false; };
-template <> struct WaveSplit<2> { static constexpr int TW = 1, SW = 2; static constexpr bool kWide = false; };
+template <> struct WaveSplit<2> { static constexpr int TW = 1, SW = 2; static constexpr bool kWide = true; };
 template <> struct WaveSplit<3> { static constexpr int TW = 3, SW = 1; static constexpr bool kWide = false; };
 template <> struct WaveSplit<4> { static constexpr int TW = 1, SW = 4; static constexpr bool kWide = true; };
 
@@ -596,9 +596,12 @@ __device__ __forceinline__ void load_query_any(Q& qf, const MqaArgs& a, int b, i
   else load_query<N, WaveSplit<N>::TW, VAR>(qf, a, b, t0, lane);
 }
 
-constexpr int kPidTable = 512;  // page ids of the next items, in LDS
+#ifndef PMQA_PID_TABLE
+#define PMQA_PID_TABLE 512
+#endif
+constexpr int kPidTable = PMQA_PID_TABLE;  // page ids of the next items, in LDS
 
-// Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+511 (up
+// Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+kPidTable-1 (up
 // to f_end); entries past the end are not written.  (b, j) is item f's
 // request and page.  Thread t walks from there to item f+t, request by
 // request (a unit spans few requests, so this is a few LDS reads).  Whole
@@ -669,7 +672,7 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
       valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
       ++issued;
       if (issued < count) {
-        if (issued % kPidTable == 0) {
+        if ((unsigned)issued % kPidTable == 0) {
           // next block of page ids; every wave gets here at the same item
           const long long f = f0 + issued;
           const int rb = locate(s_prefix, B, f);
@@ -677,7 +680,7 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
           fill_pid_table(a, s_prefix, s_pid, f, f_end, rb, (int)(f - uniform(s_prefix[rb])));
           ring_barrier();
         }
-        pid_next = uniform(s_pid[issued % kPidTable]);
+        pid_next = uniform(s_pid[(unsigned)issued % kPidTable]);
       }
     }
   };
