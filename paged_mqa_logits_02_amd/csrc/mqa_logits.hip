@@ -132,6 +132,21 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 4, 0, 0);
 }
 
+// Global loads the compiler does not track: it never inserts a wait for
+// them.  The query slice is loaded this way so that it can be issued ahead of
+// page loads and waited for with an exact count (wait_vmcnt / wait_page);
+// every use follows such a wait and settle().
+__device__ __forceinline__ v4i ldg_untracked(const void* p) {
+  v4i v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ int ldg_untracked_u8(const void* p) {
+  int v;
+  asm volatile("global_load_ubyte %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
 // Waits until at most N vector-memory loads of this wave are outstanding
 // (s_waitcnt vmcnt(N), other counters untouched).  The compiler's own waitcnt
 // tracking sees this wait; it does not track loads into LDS by itself.
@@ -227,8 +242,8 @@ template <int VAR> struct Frag;
 template <> struct Frag<0> {
   v8i v;
   __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
-    v4i lo = ldg<v4i>(row + 16 * g);
-    v4i hi = ldg<v4i>(row + 64 + 16 * g);
+    v4i lo = ldg_untracked(row + 16 * g);
+    v4i hi = ldg_untracked(row + 64 + 16 * g);
     v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
@@ -246,7 +261,7 @@ template <> struct Frag<1> {
   v4i v;
   int sf;
   __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
-    v = ldg<v4i>(row + 16 * g);
+    v = ldg_untracked(row + 16 * g);
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
     const int sw = PageLayout<1>::swz(r);
@@ -282,8 +297,8 @@ template <int VAR> struct WideFrag;
 template <> struct WideFrag<0> {
   v8i v;
   __device__ __forceinline__ void load_global(const uint8_t* row, int ks, int h) {
-    v4i lo = ldg<v4i>(row + 64 * ks + 32 * h);
-    v4i hi = ldg<v4i>(row + 64 * ks + 32 * h + 16);
+    v4i lo = ldg_untracked(row + 64 * ks + 32 * h);
+    v4i hi = ldg_untracked(row + 64 * ks + 32 * h + 16);
     v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
@@ -302,7 +317,7 @@ template <> struct WideFrag<1> {
   v4i v;
   int sf;
   __device__ __forceinline__ void load_global(const uint8_t* row, int ks, int h) {
-    v = ldg<v4i>(row + 16 * (2 * ks + h));
+    v = ldg_untracked(row + 16 * (2 * ks + h));
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
     const int c = 2 * ks + h;
@@ -327,10 +342,9 @@ template <int TW, int VAR> struct QueryFrag {
   v4f w[4][TW];        // w[mt][t][i] = weight of head 16mt + 4(l>>4) + i
 };
 
-// Forces x to be complete in its registers here: the empty asm reads and
-// redefines it, so its load is waited for at this point and code after it
-// sees a plain register value (no pending load the compiler would wait on
-// inside the page loop, where that wait would drain the page ring).
+// Marks x as redefined here: the empty asm reads and rewrites it, so no use
+// of x can be scheduled above this point.  Placed after the explicit wait for
+// the (untracked) loads of x, it makes every use see the loaded value.
 template <typename T>
 __device__ __forceinline__ void settle(T& x) {
   asm volatile("" : "+v"(x));
@@ -359,8 +373,9 @@ __device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs
     for (int mt = 0; mt < 4; ++mt) {
       const long long head_row = ((long long)(b * N + t0 + t) * 64 + 16 * mt + r);
       qf.q[mt][t].load_global(a.q + head_row * kQRow, g);
-      if constexpr (VAR == 1) qf.q[mt][t].sf = a.q_sf[head_row * 4 + g];
-      qf.w[mt][t] = ldg<v4f>(a.w + (long long)(b * N + t0 + t) * 64 + 16 * mt + 4 * g);
+      if constexpr (VAR == 1) qf.q[mt][t].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+      qf.w[mt][t] = __builtin_bit_cast(
+          v4f, ldg_untracked(a.w + (long long)(b * N + t0 + t) * 64 + 16 * mt + 4 * g));
     }
   }
 }
@@ -399,10 +414,11 @@ __device__ __forceinline__ void load_query(WideQuery<VAR>& qf, const MqaArgs& a,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       qf.q[mt][ks].load_global(a.q + head_row * kQRow, ks, h);
-      if constexpr (VAR == 1) qf.q[mt][ks].sf = a.q_sf[head_row * 4 + 2 * ks + h];
+      if constexpr (VAR == 1) qf.q[mt][ks].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + 2 * ks + h);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qf.w[mt][u] = ldg<v4f>(a.w + slot * 64 + 32 * mt + 8 * u + 4 * h);
+    for (int u = 0; u < 4; ++u)
+      qf.w[mt][u] = __builtin_bit_cast(v4f, ldg_untracked(a.w + slot * 64 + 32 * mt + 8 * u + 4 * h));
   }
 }
 
@@ -684,17 +700,28 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
       }
     }
   };
+  // The first request's query slice is loaded before the first page loads
+  // are issued, so that it is complete once page 0 is: the first wait is for
+  // page 0, not for every page in flight.
+  typename QueryOf<N, VAR>::type qf;
+  load_query_any<N, VAR>(qf, a, b, t0, lane);
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) issue_next();
+  wait_page<L::kLoadsPerWave, kAhead>(issued - 1);
+  settle_query(qf);
 
   int n = 0;
+  bool first = true;
   while (n < count && b < B) {
-    // One request: its query slice is loaded once.  It is the newest load,
-    // so waiting for it also waits for the pages in flight; this happens
-    // once per request.
-    typename QueryOf<N, VAR>::type qf;
-    load_query_any<N, VAR>(qf, a, b, t0, lane);
-    settle_query(qf);
+    // One request: its query slice is loaded once.  After the first request
+    // it is the newest load, so waiting for it also waits for the pages in
+    // flight; this happens once per request.
+    if (!first) {
+      load_query_any<N, VAR>(qf, a, b, t0, lane);
+      wait_vmcnt<0>();
+      settle_query(qf);
+    }
+    first = false;
     const int pages = min(count - n, tiles_at(s_prefix, b) - j);
     for (int k = 0; k < pages; ++k, ++n, ++j) {
       issue_next();
