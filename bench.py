@@ -7,9 +7,17 @@ rectifier, weighted head sum, s_p, store).  Inputs are resident in HBM before
 the timed region.  The KV cache is replicated and rotated so that one step's
 pages are never still in the 256 MB Infinity Cache from the previous one.
 
+Each step is launched from the host with its arguments marshalled once
+beforehand (prepared calls), so the host stays ahead of the GPU; the K timed
+steps are bracketed by one pair of HIP events on the launch stream, and the
+average launch duration is their interval over K.  --launch-events also
+brackets every launch with its own events (which can include host submission
+latency when launches are short); --graph captures the K steps into a HIP
+graph and times one replay.
+
 Prints one JSON line (rank 0, one GPU).  Usage:
   python bench.py [--steps K] [--warmup W] [--workload verify_fp8|decode_fp8|mxfp4]
-                  [--mode in_call|schedule] [--no-cpu-baseline]
+                  [--mode in_call|schedule] [--graph|--launch-events] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain copy of known size (counter scale)
 """
 import argparse
@@ -24,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KV positions/sec and achieved HBM GB/s, fp8 paged MQA logits H=64 d=128"
+METRIC_MXFP4 = "KV positions/sec and achieved HBM GB/s, mxfp4 paged MQA logits H=64 d=128"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -146,6 +155,10 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--ramp", type=float, default=1.0,
                     help="seconds of untimed launches to bring the clock up before warmup")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps into one HIP graph and time a replay")
+    ap.add_argument("--launch-events", action="store_true",
+                    help="also time every launch with its own pair of events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -186,20 +199,51 @@ def main():
     sched = torch.empty(pm.schedule_ints(U), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev0=None, ev1=None):
+    def step(i, st, ev0=None, ev1=None):
         s = None
         if args.mode == "schedule":
             pm.mqa_logits_schedule(sl, inp.next_n, variant, max_context=inp.max_context,
-                                   num_units=U, out=sched, stream=stream)
+                                   num_units=U, out=sched, stream=st)
             s = sched
         if ev0 is not None:
-            ev0.record(stream)
+            ev0.record(st)
         if variant == 0:
             pm.mqa_logits_fp8(q, kv[i % R], w, sl, bt, max_context=inp.max_context,
-                              out=outs[i % 2], schedule_meta=s, stream=stream)
+                              out=outs[i % 2], schedule_meta=s, stream=st)
         else:
             pm.mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt, max_context=inp.max_context,
-                                out=outs[i % 2], schedule_meta=s, stream=stream)
+                                out=outs[i % 2], schedule_meta=s, stream=st)
+        if ev1 is not None:
+            ev1.record(st)
+
+    # Prepared calls: the arguments of every distinct step are marshalled
+    # once, outside the timed region.
+    import math
+    L = R * 2 // math.gcd(R, 2)
+    sched_call = None
+    if args.mode == "schedule":
+        sched_call = pm.prepare_mqa_logits_schedule(sl, inp.next_n, variant,
+                                                    max_context=inp.max_context, num_units=U,
+                                                    out=sched, stream=stream)
+    calls = []
+    for i in range(L):
+        s_meta = sched if args.mode == "schedule" else None
+        if variant == 0:
+            calls.append(pm.prepare_mqa_logits_fp8(q, kv[i % R], w, sl, bt,
+                                                   max_context=inp.max_context, out=outs[i % 2],
+                                                   schedule_meta=s_meta, stream=stream))
+        else:
+            calls.append(pm.prepare_mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt,
+                                                     max_context=inp.max_context,
+                                                     out=outs[i % 2], schedule_meta=s_meta,
+                                                     stream=stream))
+
+    def fast_step(i, ev0=None, ev1=None):
+        if sched_call is not None:
+            sched_call()
+        if ev0 is not None:
+            ev0.record(stream)
+        calls[i % L]()
         if ev1 is not None:
             ev1.record(stream)
 
@@ -208,27 +252,46 @@ def main():
     t_ramp = time.time() + args.ramp
     i = 0
     while time.time() < t_ramp:
-        step(i)
+        fast_step(i)
         i += 1
         if i % 20 == 0:
             torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        fast_step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(K):
-        step(i, starts[i], ends[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if not args.graph:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              if args.launch_events else (None, None) for _ in range(K)]
+        torch.cuda.synchronize()
+        t_begin.record(stream)
+        for i in range(K):
+            fast_step(i, *ev[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        kern_ms = ([a.elapsed_time(b) for a, b in ev] if args.launch_events else [total_ms / K])
+    else:
+        # the K steps as one graph, captured on a side stream (default
+        # priority), replayed once untimed and once timed on the launch stream
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(i, cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t_begin.record(stream)
+        graph.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        kern_ms = [total_ms / K]
     kern_avg = float(np.mean(kern_ms))
 
     traffic = counter_traffic(args.workload)
@@ -239,7 +302,7 @@ def main():
     value = positions * K / (total_ms * 1e-3)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if variant == 0 else METRIC_MXFP4,
         "value": value,
         "unit": "KV positions/s",
         "n_gpus": 1,
@@ -259,6 +322,10 @@ def main():
             "head_dim": inp.head_dim, "max_context": inp.max_context,
             "kv_positions": positions, "pages": int(inp.num_pages),
             "schedule": args.mode, "kv_replicas": R, "units": U,
+            "timing": ("graph of the %d steps, events around one replay" % K if args.graph else
+                       "host launches of prepared calls, " +
+                       ("events around every launch" if args.launch_events else
+                        "events around the %d launches" % K)),
             "kernel_ms_avg": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
             "algorithmic_bytes_per_position": bpp,
             "algorithmic_bytes_per_launch": alg_bytes,

@@ -155,19 +155,31 @@ def mqa_logits_schedule(seq_lens: torch.Tensor, next_n: int, variant: int = VARI
     """Builds the opaque work split on the GPU (int32 tensor).  Valid only
     while seq_lens is unchanged; pass the same next_n/variant/max_context to
     the logits call."""
-    if num_units == 0:
-        num_units = globals()["num_units"](next_n, variant, seq_lens.device.index)
-    n = schedule_ints(num_units)
+    out, args = _schedule_args(seq_lens, next_n, variant, max_context, num_units, out, stream)
+    _check(_lib.mqa_logits_schedule(*args), "mqa_logits_schedule")
+    return out
+
+
+def _schedule_args(seq_lens, next_n, variant, max_context, num_units_, out, stream):
+    if num_units_ == 0:
+        num_units_ = num_units(next_n, variant, seq_lens.device.index)
+    n = schedule_ints(num_units_)
     if n < 0:
         raise PmqaError(-2, "mqa_logits_schedule")
     if out is None:
         out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
     elif out.numel() < n or out.dtype != torch.int32:
         raise ValueError("schedule buffer too small")
-    _check(_lib.mqa_logits_schedule(_ptr(seq_lens), seq_lens.shape[0], next_n, variant,
-                                    max_context, num_units, _ptr(out),
-                                    _stream(stream, seq_lens.device)), "mqa_logits_schedule")
-    return out
+    return out, (_ptr(seq_lens), seq_lens.shape[0], next_n, variant, max_context, num_units_,
+                 _ptr(out), _stream(stream, seq_lens.device))
+
+
+def prepare_mqa_logits_schedule(seq_lens: torch.Tensor, next_n: int, variant: int = VARIANT_FP8,
+                                *, max_context: int, num_units: int = 0,
+                                out: torch.Tensor = None, stream=None):
+    """mqa_logits_schedule with its arguments marshalled once; returns a PreparedCall."""
+    out, args = _schedule_args(seq_lens, next_n, variant, max_context, num_units, out, stream)
+    return PreparedCall(_lib.mqa_logits_schedule, args, "mqa_logits_schedule", out, (seq_lens,))
 
 
 # ---------------------------------------------------------------- operations
@@ -187,6 +199,23 @@ def _dtype_code(dtype):
     raise ValueError("unsupported output dtype %s" % dtype)
 
 
+def _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
+              schedule_meta, output_dtype, acc_dtype, stream):
+    B, N, H, D = q.shape
+    if next_n is not None and next_n != N:
+        raise ValueError("next_n does not match q")
+    bt_stride, bt_width = _rows_of(block_table)
+    if max_context is None:
+        max_context = out.shape[1] if out is not None else bt_width * PAGE
+    out = _out_for(out, B * N, max_context, output_dtype, q.device)
+    ors, _ = _rows_of(out)
+    ps, npages = _pages(kv_fused)
+    acc = _dtype_code(acc_dtype) if acc_dtype in (torch.float32, torch.bfloat16) else 99
+    return out, (_ptr(q), _ptr(kv_fused), ps, npages, _ptr(weights), _ptr(seq_lens),
+                 _ptr(block_table), bt_stride, bt_width, B, N, H, D, _ptr(out), ors, max_context,
+                 _dtype_code(out.dtype), acc, _ptr(schedule_meta), _stream(stream, q.device))
+
+
 def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                    max_context=None, out=None, schedule_meta=None,
                    output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
@@ -198,7 +227,15 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
     [batch, width] int32.  Columns at or beyond ceil(seq_len/64)*64 and rows
     of empty requests are not written (out=None allocates uninitialised
     memory)."""
-    B, N, H, D = q.shape
+    out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
+                          schedule_meta, output_dtype, acc_dtype, stream)
+    _check(_lib.mqa_logits_fp8(*args), "mqa_logits_fp8")
+    return out
+
+
+def _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n, sf_vec_size,
+                is_kv_sf_interleaved, max_context, out, schedule_meta, output_dtype, stream):
+    B, N, H, Dh = q.shape
     if next_n is not None and next_n != N:
         raise ValueError("next_n does not match q")
     bt_stride, bt_width = _rows_of(block_table)
@@ -207,13 +244,10 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
     out = _out_for(out, B * N, max_context, output_dtype, q.device)
     ors, _ = _rows_of(out)
     ps, npages = _pages(kv_fused)
-    acc = _dtype_code(acc_dtype) if acc_dtype in (torch.float32, torch.bfloat16) else 99
-    _check(_lib.mqa_logits_fp8(_ptr(q), _ptr(kv_fused), ps, npages, _ptr(weights),
-                               _ptr(seq_lens), _ptr(block_table), bt_stride, bt_width, B, N, H,
-                               D, _ptr(out), ors, max_context, _dtype_code(out.dtype), acc,
-                               _ptr(schedule_meta), _stream(stream, q.device)),
-           "mqa_logits_fp8")
-    return out
+    return out, (_ptr(q), _ptr(q_sf), sf_vec_size, int(is_kv_sf_interleaved), _ptr(kv_fused), ps,
+                 npages, _ptr(weights), _ptr(seq_lens), _ptr(block_table), bt_stride, bt_width,
+                 B, N, H, Dh * 2, _ptr(out), ors, max_context, _dtype_code(out.dtype),
+                 _ptr(schedule_meta), _stream(stream, q.device))
 
 
 def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=None, *,
@@ -224,22 +258,51 @@ def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=N
     q [batch, next_n, 64, 64] packed e2m1 uint8; q_sf [batch, next_n, 64, 4]
     e8m0 uint8; kv_fused [pages, page_bytes] uint8 with 64x64 packed key bytes
     then 64x4 e8m0 codes per page."""
-    B, N, H, Dh = q.shape
-    if next_n is not None and next_n != N:
-        raise ValueError("next_n does not match q")
-    bt_stride, bt_width = _rows_of(block_table)
-    if max_context is None:
-        max_context = out.shape[1] if out is not None else bt_width * PAGE
-    out = _out_for(out, B * N, max_context, output_dtype, q.device)
-    ors, _ = _rows_of(out)
-    ps, npages = _pages(kv_fused)
-    _check(_lib.mqa_logits_mxfp4(_ptr(q), _ptr(q_sf), sf_vec_size, int(is_kv_sf_interleaved),
-                                 _ptr(kv_fused), ps, npages, _ptr(weights), _ptr(seq_lens),
-                                 _ptr(block_table), bt_stride, bt_width, B, N, H, Dh * 2,
-                                 _ptr(out), ors, max_context, _dtype_code(out.dtype),
-                                 _ptr(schedule_meta), _stream(stream, q.device)),
-           "mqa_logits_mxfp4")
+    out, args = _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n,
+                            sf_vec_size, is_kv_sf_interleaved, max_context, out, schedule_meta,
+                            output_dtype, stream)
+    _check(_lib.mqa_logits_mxfp4(*args), "mqa_logits_mxfp4")
     return out
+
+
+class PreparedCall:
+    """One library call with its arguments marshalled once (device pointers,
+    sizes, stream).  Calling it enqueues the same call again on the same
+    stream; the tensors it was prepared from are kept alive and must keep
+    their storage.  For launch-rate-bound callers (short calls issued from a
+    host loop)."""
+
+    def __init__(self, fn, args, where, out, keep):
+        self._fn, self._args, self._where, self.out = fn, args, where, out
+        self._keep = keep  # the tensors whose device pointers are in args
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            raise PmqaError(rc, self._where)
+        return self.out
+
+
+def prepare_mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
+                           max_context=None, out=None, schedule_meta=None,
+                           output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
+    """mqa_logits_fp8 with its arguments marshalled once; returns a PreparedCall."""
+    out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
+                          schedule_meta, output_dtype, acc_dtype, stream)
+    return PreparedCall(_lib.mqa_logits_fp8, args, "mqa_logits_fp8", out,
+                        (q, kv_fused, weights, seq_lens, block_table, schedule_meta))
+
+
+def prepare_mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=None, *,
+                             sf_vec_size=32, is_kv_sf_interleaved=False, max_context=None,
+                             out=None, schedule_meta=None, output_dtype=torch.bfloat16,
+                             stream=None):
+    """mqa_logits_mxfp4 with its arguments marshalled once; returns a PreparedCall."""
+    out, args = _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n,
+                            sf_vec_size, is_kv_sf_interleaved, max_context, out, schedule_meta,
+                            output_dtype, stream)
+    return PreparedCall(_lib.mqa_logits_mxfp4, args, "mqa_logits_mxfp4", out,
+                        (q, q_sf, kv_fused, weights, seq_lens, block_table, schedule_meta))
 
 
 def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,

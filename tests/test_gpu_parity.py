@@ -328,3 +328,31 @@ def test_poisoned_unread_data_never_reaches_outputs():
     got, wrote = host_out(dm.run())
     assert not np.isnan(got[wrote]).any()
     check_dense(dm, dm.run(), "poisoned")
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+def test_prepared_call_matches_direct_call(variant):
+    """A PreparedCall (arguments marshalled once) issues the same call: its
+    output is bit-identical to the direct call's, with and without a
+    schedule, on every repeat."""
+    inp = _mid_inputs(variant, next_n=2, seed=310)
+    dm = DevMqa(inp)
+    ref, _ = host_out(dm.run())
+    m = pm()
+    v = 0 if variant == "fp8" else 1
+    sched_call = m.prepare_mqa_logits_schedule(dm.sl, inp.next_n, v, max_context=inp.max_context)
+    for schedule in (None, sched_call.out):
+        out = dm.new_out()
+        if variant == "fp8":
+            call = m.prepare_mqa_logits_fp8(dm.q, dm.kv, dm.w, dm.sl, dm.bt,
+                                            max_context=inp.max_context, out=out,
+                                            schedule_meta=schedule)
+        else:
+            call = m.prepare_mqa_logits_mxfp4(dm.q, dm.q_sf, dm.kv, dm.w, dm.sl, dm.bt,
+                                              max_context=inp.max_context, out=out,
+                                              schedule_meta=schedule)
+        for _ in range(2):
+            if schedule is not None:
+                sched_call()
+            got, _ = host_out(call())
+            assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
