@@ -16,18 +16,18 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kPage = 64;   // tokens per KV page
 constexpr int kWave = 64;   // lanes per wavefront
-constexpr int kE8M0One = 127;  // e8m0 code of 1.0
 
 constexpr int kFmtFp8 = 0;  // cbsz/blgp operand format: e4m3
 constexpr int kFmtFp4 = 4;  // cbsz/blgp operand format: e2m1
 
-// D[16x16] = A[16x128] * B[128x16] (+ C), e4m3 operands, fp32 accumulate.
+// D[16x16] = A[16x128] * B[128x16] (+ C), e4m3 operands, fp32 accumulate,
+// no block scales (zero scale operands select the unscaled instruction; the
+// parity tests confirm the products are unscaled).
 // Lane l holds row (l & 15) of A / column (l & 15) of B and 32 of the 128 K
 // values, in the same slots for A and B.  Output lane l, element i is
 // D[4*(l>>4) + i][l & 15].
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, kE8M0One,
-                                                          0, kE8M0One);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, 0, 0, 0);
 }
 
 // Same shape with e2m1 operands (32 values = 16 bytes per lane) and one e8m0
@@ -39,13 +39,13 @@ __device__ __forceinline__ v4f mfma_fp4(const v4i& a, int sa, const v4i& b, int 
                                                           sb);
 }
 
-// D[32x32] = A[32x64] * B[64x32] (+ C), e4m3 operands, fp32 accumulate.
+// D[32x32] = A[32x64] * B[64x32] (+ C), e4m3 operands, fp32 accumulate, no
+// block scales.
 // Lane l holds row (l & 31) of A / column (l & 31) of B and 32 of the 64 K
 // values, in the same slots for A and B.  Output lane l, element i is
 // D[8*(i>>2) + 4*(l>>5) + (i&3)][l & 31].
 __device__ __forceinline__ v16f mfma32_fp8(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, kE8M0One,
-                                                         0, kE8M0One);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtFp8, kFmtFp8, 0, 0, 0, 0);
 }
 
 // Same shape with e2m1 operands (32 values = 16 bytes per lane) and one e8m0
