@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV positions/sec and achieved HBM GB/s, fp8 paged MQA logits H=64 d=128"
 METRIC_MXFP4 = "KV positions/sec and achieved HBM GB/s, mxfp4 paged MQA logits H=64 d=128"
+METRIC_INDEXER = "KV positions/sec and achieved HBM GB/s, one-head bf16 indexer scores d=128"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -40,6 +41,8 @@ WORKLOADS = {
     "verify_fp8": "B=128, next_n=4, H=64, d=128, page 64, seq_lens uniform 4K..64K, fp32 out",
     "decode_fp8": "B=64, next_n=1, H=64, d=128, page 64, seq_lens log-uniform 1K..32K, fp32 out",
     "mxfp4": "B=64, next_n=2, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
+    "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
+                    "context lengths uniform 0..4096 (one 0), fp32 scores",
 }
 
 
@@ -145,13 +148,76 @@ def copy_calibration(steps):
                       "gb_per_s": 2 * n / dt / 1e9}))
 
 
+def run_indexer(args, torch, synth, pm, dev):
+    """The one-head BF16 indexer workload: one indexer_scores call per step."""
+    inp = synth.make_config("indexer_bf16")
+    key_bytes = inp.key_cache.nbytes
+    R = args.replicas or max(2, -(-2 * MALL_BYTES // key_bytes))
+    keys = [torch.from_numpy(inp.key_cache).to(dev) for _ in range(R)]
+    qry = torch.from_numpy(inp.query.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.context_lengths).to(dev)
+    reqs = torch.from_numpy(inp.requests).to(dev)
+    offs = None if inp.group_row_offsets is None else torch.from_numpy(inp.group_row_offsets).to(dev)
+    scores = [torch.empty((inp.rows, inp.max_context), dtype=torch.float32, device=dev)
+              for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    import math
+    L = R * 2 // math.gcd(R, 2)
+    calls = [pm.prepare_indexer_scores(qry, keys[i % R], bt, lens, requests=reqs,
+                                       scores=scores[i % 2], group_row_offsets=offs,
+                                       stream=stream) for i in range(L)]
+    t_ramp = time.time() + args.ramp
+    i = 0
+    while time.time() < t_ramp:
+        calls[i % L]()
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    for i in range(args.warmup):
+        calls[i % L]()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        calls[i % L]()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern = total_ms / K
+    lens_np = np.minimum(np.maximum(inp.context_lengths, 0), inp.max_context).astype(np.int64)
+    sizes = np.diff(inp.row_offsets()).astype(np.int64)
+    alg = int((lens_np * (256 + 4 * sizes)).sum())  # key bytes + one score per row, per key
+    positions = int(lens_np.sum())
+    achieved = alg / (kern * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_INDEXER, "value": positions * K / (total_ms * 1e-3),
+        "unit": "KV positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": kern, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "gb_per_s": achieved,
+        "config": {"workload": "indexer_bf16", "shape": WORKLOADS["indexer_bf16"],
+                   "rows": inp.rows, "groups": inp.groups, "max_context": inp.max_context,
+                   "kv_positions": positions, "key_replicas": R, "kernel_ms_avg": kern,
+                   "timing": "host launches of prepared calls, events around the %d launches" % K,
+                   "algorithmic_bytes_per_launch": alg},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="verify_fp8", choices=sorted(WORKLOADS))
-    ap.add_argument("--mode", default="in_call", choices=["in_call", "schedule"])
+    ap.add_argument("--mode", default="in_call", choices=["in_call", "schedule", "reuse"],
+                    help="work split: inside the logits kernel; by the schedule kernel every "
+                         "step; or one schedule computed before the timed steps and reused")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--ramp", type=float, default=1.0,
                     help="seconds of untimed launches to bring the clock up before warmup")
@@ -180,6 +246,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pm.init(0)
+    if args.workload == "indexer_bf16":
+        run_indexer(args, torch, synth, pm, dev)
+        return
     inp = synth.make_config(args.workload)
     variant = 0 if inp.variant == "fp8" else 1
     out_dtype = torch.float32 if inp.out_dtype == "f32" else torch.bfloat16
@@ -200,7 +269,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(i, st, ev0=None, ev1=None):
-        s = None
+        s = sched if args.mode == "reuse" else None
         if args.mode == "schedule":
             pm.mqa_logits_schedule(sl, inp.next_n, variant, max_context=inp.max_context,
                                    num_units=U, out=sched, stream=st)
@@ -221,13 +290,14 @@ def main():
     import math
     L = R * 2 // math.gcd(R, 2)
     sched_call = None
-    if args.mode == "schedule":
+    if args.mode != "in_call":
         sched_call = pm.prepare_mqa_logits_schedule(sl, inp.next_n, variant,
                                                     max_context=inp.max_context, num_units=U,
                                                     out=sched, stream=stream)
+        sched_call()  # the reused schedule; recomputed every step in "schedule" mode
     calls = []
     for i in range(L):
-        s_meta = sched if args.mode == "schedule" else None
+        s_meta = sched if args.mode != "in_call" else None
         if variant == 0:
             calls.append(pm.prepare_mqa_logits_fp8(q, kv[i % R], w, sl, bt,
                                                    max_context=inp.max_context, out=outs[i % 2],
@@ -239,7 +309,7 @@ def main():
                                                      stream=stream))
 
     def fast_step(i, ev0=None, ev1=None):
-        if sched_call is not None:
+        if args.mode == "schedule":
             sched_call()
         if ev0 is not None:
             ev0.record(stream)

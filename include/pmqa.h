@@ -170,8 +170,10 @@ int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, 
 /* Number of int32 entries of a schedule buffer for num_units units. */
 int64_t mqa_logits_schedule_ints(int32_t num_units);
 
-/* The unit count a NULL-schedule call of this configuration uses on `device`
- * (waves resident on the whole GPU); < 0 on error. */
+/* The unit count a NULL-schedule call of this configuration uses on `device`:
+ * the workgroups resident on the whole GPU, one contiguous range each (for a
+ * batch with a short seq_lens prefix); < 0 on error.  A schedule built with
+ * this count gives each workgroup one range, like the in-call split. */
 int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant);
 
 /* Columns written per row for a request of seq_len tokens: ceil(seq_len/64)*64

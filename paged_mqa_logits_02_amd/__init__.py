@@ -313,13 +313,29 @@ def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, 
     uint8 (pages may be strided views); block_table [requests, width] int32;
     context_lengths / requests [groups] int32; group_row_offsets optional
     [groups+1] int32 (None: rows/groups rows per group)."""
+    args = _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
+                         group_row_offsets, stream)
+    _check(_lib.indexer_scores(*args), "indexer_scores")
+    return scores
+
+
+def _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
+                  group_row_offsets, stream):
     rows, D = query.shape
     bt_stride, bt_width = _rows_of(block_table)
     srs, max_context = _rows_of(scores)
     ps, npages = _pages(key_cache)
-    _check(_lib.indexer_scores(_ptr(query), rows, D, _ptr(key_cache), ps, npages,
-                               _ptr(block_table), bt_stride, bt_width, block_table.shape[0],
-                               _ptr(context_lengths), _ptr(requests), context_lengths.shape[0],
-                               _ptr(group_row_offsets), _ptr(scores), srs, max_context,
-                               _stream(stream, query.device)), "indexer_scores")
-    return scores
+    return (_ptr(query), rows, D, _ptr(key_cache), ps, npages, _ptr(block_table), bt_stride,
+            bt_width, block_table.shape[0], _ptr(context_lengths), _ptr(requests),
+            context_lengths.shape[0], _ptr(group_row_offsets), _ptr(scores), srs, max_context,
+            _stream(stream, query.device))
+
+
+def prepare_indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,
+                           group_row_offsets=None, stream=None):
+    """indexer_scores with its arguments marshalled once; returns a PreparedCall."""
+    args = _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
+                         group_row_offsets, stream)
+    return PreparedCall(_lib.indexer_scores, args, "indexer_scores", scores,
+                        (query, key_cache, block_table, context_lengths, requests,
+                         group_row_offsets))

@@ -257,8 +257,10 @@ int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant) {
   if (rc != PMQA_OK) return rc;
   const DeviceInfo& d = g_dev[device];
   const int out = variant == PMQA_VARIANT_FP8 ? 0 : 1;  // the variant's default output
+  // one unit per resident workgroup: a workgroup pays the start-up of a range
+  // (page ids, first page loads, query) once per unit
   const size_t lds = mqa_ring_bytes(variant) + sizeof(int);
-  return d.cus * blocks_per_cu(d, next_n, variant, out, lds) * (kBlockThreads / 64);
+  return d.cus * blocks_per_cu(d, next_n, variant, out, lds);
 }
 
 int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,
