@@ -1,0 +1,67 @@
+"""Code-generation guard for the logits kernels (CPU: hipcc cross-compiles).
+
+The page loop waits for page loads with exact vmcnt counts.  If any load the
+compiler tracks stays pending on a path into the loop, the compiler inserts
+`s_waitcnt vmcnt(0)` before the page's LDS operand reads, which drains the
+whole page ring on every page (this happened once and cost 10-20% on the long
+workloads with correct results).  The test compiles the kernels to gfx950
+assembly with the library's own flags and checks that no basic block holding
+a matrix instruction waits for vmcnt(0) before its first one."""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def drains_before_mfma(asm):
+    bad = []
+    kernels = re.findall(r"^(_ZN4pmqa17mqa_logits_kernel\S+):[^\n]*\n(.*?)^\s+s_endpgm", asm,
+                         re.S | re.M)
+    assert kernels, "no logits kernels found in the assembly"
+    for name, body in kernels:
+        for blk in re.split(r"^(?=\.LBB\S+:|; %bb\.\d+:)", body, flags=re.M):
+            if "v_mfma" in blk and re.search(r"s_waitcnt\s+vmcnt\(0\)",
+                                             blk[:blk.index("v_mfma")]):
+                bad.append(name)
+    return kernels, bad
+
+
+def test_page_loop_has_no_full_drain_before_the_matrix_work():
+    import sys
+    sys.path.insert(0, ROOT)
+    from paged_mqa_logits_02_amd import build
+    try:
+        cc = build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    src = os.path.join(build.CSRC, "mqa_logits.hip")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        flags = [f for f in build.compile_flags("mqa_logits.hip") if f != "-fPIC"]
+        r = subprocess.run([cc] + flags + ["--cuda-device-only", "-S", src, "-o", out],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        asm = open(out).read()
+    kernels, bad = drains_before_mfma(asm)
+    assert len(kernels) == 16  # next_n 1..4 x {fp8, mxfp4} x {fp32, bf16 out}
+    assert not bad, "vmcnt(0) before the matrix work in: %s" % sorted(set(bad))
+
+
+def test_guard_detects_a_drain():
+    asm = """_ZN4pmqa17mqa_logits_kernelILi4ELi0ELi0EEEvX:   ; @k
+.LBB0_1:                                ; in Loop
+\ts_barrier
+\ts_waitcnt vmcnt(0)
+\tds_read_b128 v[0:3], v4
+\tv_mfma_f32_32x32x64_f8f6f4 v[10:25], v[34:41], v[0:7], 0
+\ts_endpgm
+"""
+    _, bad = drains_before_mfma(asm)
+    assert bad
+    _, ok = drains_before_mfma(asm.replace("vmcnt(0)", "vmcnt(6)"))
+    assert not ok

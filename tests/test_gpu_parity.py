@@ -13,7 +13,7 @@ import oracle
 import synth
 from fixtures_util import (extent, indexer_from_case, load_golden, mqa_from_case)
 from gpu_util import (DEV, DevIndexer, DevMqa, check_dense, check_indexer, check_sampled,
-                      host_out, pm, say)
+                      check_values, host_out, pm, say, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -356,3 +356,43 @@ def test_prepared_call_matches_direct_call(variant):
                 sched_call()
             got, _ = host_out(call())
             assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+def test_out_of_range_page_id_gives_nan_for_that_page_only(variant):
+    """A block-table entry outside [0, num_pages) is never dereferenced: the
+    outputs of that page (every slot row of the request, the page's 64
+    columns) are NaN, and every other written cell is as with a valid table."""
+    inp = _mid_inputs(variant, next_n=2, seed=311)
+    tiles = np.where(inp.seq_lens > 0, (inp.seq_lens + 63) // 64, 0)
+    b1, b2 = [int(b) for b in np.nonzero(tiles >= 3)[0][:2]]
+    bad = copy.copy(inp)
+    bad.block_table = inp.block_table.copy()
+    bad.block_table[b1, 1] = inp.num_pages + 7
+    bad.block_table[b2, 2] = -5
+    out = DevMqa(bad).run()
+    got, wrote = host_out(out)
+    ref, amag, written = oracle.mqa_logits_for(inp)
+    assert np.array_equal(wrote, written)
+    N = inp.next_n
+    poison = np.zeros_like(written)
+    poison[b1 * N:(b1 + 1) * N, 64:128] = True
+    poison[b2 * N:(b2 + 1) * N, 128:192] = True
+    assert np.array_equal(poison & written, poison)
+    assert np.isnan(got[poison]).all()
+    ok = written & ~poison
+    check_values(got[ok], ref[ok], amag[ok], tol_for(out.dtype), "valid pages")
+
+
+def test_largest_batch():
+    """B = 8192 requests, the largest batch the entry points accept (the
+    per-request page-count prefix then fills 32 KB of LDS): complete written
+    set, sampled values, in-call split and schedule."""
+    rng = np.random.default_rng(312)
+    lens = rng.integers(0, 300, 8192)
+    lens[::97] = 0
+    inp = synth.make_mqa_inputs(lens, 1, max_context=320, bt_width=5, seed=312)
+    dm = DevMqa(inp)
+    check_sampled(dm, dm.run(), np.random.default_rng(5), "in-call")
+    sched = pm().mqa_logits_schedule(dm.sl, 1, 0, max_context=inp.max_context)
+    check_sampled(dm, dm.run(schedule=sched), np.random.default_rng(6), "schedule")
