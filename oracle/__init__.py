@@ -13,8 +13,10 @@ Which passage each function follows:
                             introductory equation, the bullets on the per-head
                             rectifier and on s_p / MXFP4 block scales, and the
                             output-contract note.
-  * ``indexer_scores``    - FlashInfer "flashinfer.sdsa.indexer_scores":
-                            description and parameter list.
+  * ``indexer_scores`` / ``indexer_scores_nvfp4`` - FlashInfer
+                            "flashinfer.sdsa.indexer_scores": description and
+                            parameter list (BF16 inputs; NVFP4 inputs with
+                            query_scales / key_scales).
   * ``e4m3``/``e2m1``/``e8m0``/``bf16`` - OCP 8-bit FP and OCP MX v1.0
                             format definitions.
 """
@@ -60,6 +62,8 @@ def _load():
             lib.oracle_mqa_written.argtypes = [P, I32, I32, I32, P]
             lib.oracle_indexer_scores.argtypes = [P, I32, I32, P, I64, P, I64, P, P, P, I32, I32,
                                                   P, P, P, ctypes.c_int]
+            lib.oracle_indexer_scores_nvfp4.argtypes = [P, P, I32, I32, P, I64, P, I64, P, I64,
+                                                        P, P, P, I32, I32, P, P, P, ctypes.c_int]
             for f in ("oracle_e4m3", "oracle_e2m1", "oracle_e8m0"):
                 getattr(lib, f).argtypes = [ctypes.c_uint8]
                 getattr(lib, f).restype = ctypes.c_double
@@ -202,7 +206,38 @@ def indexer_scores(query, key_cache, page_stride, block_table, context_lengths, 
     return ref, amag, written.astype(bool)
 
 
+def indexer_scores_nvfp4(query, query_scales, key_cache, page_stride, key_scales,
+                         scale_page_stride, block_table, context_lengths, requests, row_offsets,
+                         max_context, nthreads=None):
+    """Dense oracle for NVFP4 query and keys (packed e2m1, e4m3 scale per 16
+    values).  Returns (ref, amag, written), each [rows, max_context]."""
+    lib = _load()
+    q = _c(query, np.uint8)
+    rows, half = q.shape
+    qs = _c(query_scales, np.uint8)
+    kc, ks = _c(key_cache, np.uint8), _c(key_scales, np.uint8)
+    bt = _c(block_table, np.int32)
+    cl, rq, ro = _c(context_lengths, np.int32), _c(requests, np.int32), _c(row_offsets, np.int32)
+    groups = cl.shape[0]
+    ref = np.full((rows, max_context), np.nan)
+    amag = np.zeros((rows, max_context))
+    written = np.zeros((rows, max_context), dtype=np.uint8)
+    rc = lib.oracle_indexer_scores_nvfp4(_ptr(q), _ptr(qs), rows, 2 * half, _ptr(kc),
+                                         int(page_stride), _ptr(ks), int(scale_page_stride),
+                                         _ptr(bt), int(bt.shape[1]), _ptr(cl), _ptr(rq), _ptr(ro),
+                                         groups, max_context, _ptr(ref), _ptr(amag),
+                                         _ptr(written), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_indexer_scores_nvfp4: bad arguments (%d)" % rc)
+    return ref, amag, written.astype(bool)
+
+
 def indexer_scores_for(inp, nthreads=None):
+    if getattr(inp, "fmt", "bf16") == "nvfp4":
+        return indexer_scores_nvfp4(inp.query, inp.query_scales, inp.key_cache, inp.page_stride,
+                                    inp.key_scales, inp.scale_page_stride, inp.block_table,
+                                    inp.context_lengths, inp.requests, inp.row_offsets(),
+                                    inp.max_context, nthreads)
     return indexer_scores(inp.query, inp.key_cache, inp.page_stride, inp.block_table,
                           inp.context_lengths, inp.requests, inp.row_offsets(),
                           inp.max_context, nthreads)

@@ -19,7 +19,9 @@
  *   [indexer]       "flashinfer.sdsa.indexer_scores": one head, so a score is
  *                   the plain dot product of a query row and a key; pages of
  *                   64 keys; scores[q,k] is written for k below the group's
- *                   length and not beyond.
+ *                   length and not beyond; BF16 inputs, or NVFP4 inputs
+ *                   (packed e2m1 with an e4m3 scale per 16 values, the key
+ *                   scales paged like the keys).
  *
  * Readings taken where the pages are silent (each is listed in the design notes):
  *   - the scheduled extent of every row of request b is the request's length
@@ -362,6 +364,68 @@ int oracle_indexer_scores(const uint16_t* query, int32_t rows, int32_t D, const 
                 int d;
                 for (d = 0; d < D; ++d) {
                     double prod = oracle_bf16(query[(int64_t)r * D + d]) * oracle_bf16(key[d]);
+                    dot += prod;
+                    mag += fabs(prod);
+                }
+                scores[(int64_t)r * max_context + k] = dot;
+                amag[(int64_t)r * max_context + k] = mag;
+                written[(int64_t)r * max_context + k] = 1;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * One-head indexer scores with NVFP4 inputs ([indexer], query / key_cache /
+ * query_scales / key_scales parameters): the query is packed e2m1
+ * [rows, D/2] with one e4m3 scale per 16 values in query_scales [rows, D/16];
+ * each key page holds 64 keys of packed e2m1 [64, D/2] at its start, and the
+ * page's e4m3 scales [64, D/16] sit at key_scales + page*scale_page_stride
+ * ("paged like the keys").  A score is the dot product of the dequantised
+ * vectors: sum_d (e2m1(q_d) * qs[d/16]) * (e2m1(k_d) * ks[d/16]).  Packed
+ * bytes hold the even element in the low nibble.  amag = sum_d |q_d k_d| of
+ * the dequantised values.  Same extent and group rules as the BF16 form.
+ */
+static double nvfp4_at(const uint8_t* packed, const uint8_t* scales, int d)
+{
+    uint8_t byte = packed[d / 2];
+    uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+    return oracle_e2m1(nib) * oracle_e4m3(scales[d / 16]);
+}
+
+int oracle_indexer_scores_nvfp4(const uint8_t* query, const uint8_t* query_scales, int32_t rows,
+                                int32_t D, const uint8_t* key_cache, int64_t page_stride,
+                                const uint8_t* key_scales, int64_t scale_page_stride,
+                                const int32_t* bt, int64_t bt_stride,
+                                const int32_t* context_lengths, const int32_t* requests,
+                                const int32_t* row_offsets, int32_t groups, int32_t max_context,
+                                double* scores, double* amag, uint8_t* written, int nthreads)
+{
+    int32_t g;
+    (void)nthreads;
+    if (rows < 0 || groups < 0 || D < 16 || D % 16 != 0 || max_context < 0)
+        return -2;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (g = 0; g < groups; ++g) {
+        int32_t L = context_lengths[g], r;
+        int64_t k;
+        if (L > max_context)
+            L = max_context;
+        if (L <= 0)
+            continue;
+        for (r = row_offsets[g]; r < row_offsets[g + 1]; ++r) {
+            const uint8_t* qrow = query + (int64_t)r * (D / 2);
+            const uint8_t* qsc = query_scales + (int64_t)r * (D / 16);
+            for (k = 0; k < L; ++k) {
+                int32_t page = bt[(int64_t)requests[g] * bt_stride + k / TOK_PER_PAGE];
+                int64_t j = k % TOK_PER_PAGE;
+                const uint8_t* krow = key_cache + (int64_t)page * page_stride + j * (D / 2);
+                const uint8_t* ksc = key_scales + (int64_t)page * scale_page_stride + j * (D / 16);
+                double dot = 0.0, mag = 0.0;
+                int d;
+                for (d = 0; d < D; ++d) {
+                    double prod = nvfp4_at(qrow, qsc, d) * nvfp4_at(krow, ksc, d);
                     dot += prod;
                     mag += fabs(prod);
                 }

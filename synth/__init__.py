@@ -45,6 +45,15 @@ def encode_e4m3(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """uint8 e4m3fn codes -> float32 values (used only to quantise against a
+    scale that is itself stored as e4m3)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
 def encode_bf16(x: np.ndarray) -> np.ndarray:
     """float32 array -> uint16 bf16 bit patterns (RNE)."""
     import torch
@@ -98,6 +107,31 @@ def quantize_mxfp4(x: np.ndarray):
     nib = nib.reshape(x.shape)
     packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
     return packed, code.astype(np.uint8)
+
+
+def quantize_nvfp4(x: np.ndarray):
+    """NVFP4 quantisation with 16-element blocks along the last axis.
+
+    block scale = amax/6 (e2m1's largest magnitude) encoded as e4m3 (1.0 for
+    an all-zero block); elements divided by the decoded scale, rounded to
+    nearest even on the e2m1 grid and clamped to +-6.
+    Returns (packed uint8 [..., D/2], e4m3 scale codes uint8 [..., D/16]).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    assert D % 16 == 0
+    xb = x.reshape(x.shape[:-1] + (D // 16, 16))
+    amax = np.max(np.abs(xb), axis=-1)
+    code = encode_e4m3(np.where(amax > 0, amax / np.float32(6.0), np.float32(1.0)))
+    scale = decode_e4m3(code)
+    v = np.abs(xb) / scale[..., None]
+    idx = np.zeros(v.shape, dtype=np.uint8)
+    for mid, up in zip(_E2M1_MIDS, _E2M1_TIE_UP):
+        idx += (v >= mid) if up else (v > mid)
+    nib = idx | (np.signbit(xb).astype(np.uint8) << 3)
+    nib = nib.reshape(x.shape)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, code
 
 
 # --------------------------------------------------------------------------
@@ -227,6 +261,12 @@ class IndexerInputs:
     group_row_offsets: Optional[np.ndarray]  # i32 [groups+1] or None (uniform)
     max_context: int
     name: str = ""
+    # NVFP4 inputs: query u8 [rows, 64] packed e2m1 and key pages u8 [64, 64]
+    # packed e2m1 at offset 0 of each key_cache page; e4m3 scales per 16 values
+    fmt: str = "bf16"
+    query_scales: Optional[np.ndarray] = None  # u8 [rows, 8]
+    key_scales: Optional[np.ndarray] = None  # u8 [pages, scale_page_stride] ([64, 8] at offset 0)
+    scale_page_stride: int = 0
 
     @property
     def rows(self) -> int:
@@ -249,7 +289,7 @@ class IndexerInputs:
 def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=4096,
                         group_sizes=None, uniform_group=None, max_len=4096,
                         zero_group=True, seed=2, page_stride=None, head_dim=128,
-                        name="") -> IndexerInputs:
+                        name="", fmt="bf16", scale_page_stride=None) -> IndexerInputs:
     rng = np.random.default_rng(seed)
     if uniform_group is not None:
         assert rows % uniform_group == 0
@@ -265,12 +305,28 @@ def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=409
     assert sum(sizes) == rows and all(1 <= g <= 8 for g in sizes)
     groups = len(sizes)
     num_pages = num_requests * bt_width
-    if page_stride is None:
-        page_stride = PAGE * head_dim * 2
-    q = encode_bf16(rng.standard_normal((rows, head_dim), dtype=np.float32))
-    keys = encode_bf16(rng.standard_normal((num_pages, PAGE, head_dim), dtype=np.float32))
-    key_cache = np.zeros((num_pages, page_stride), dtype=np.uint8)
-    key_cache[:, : PAGE * head_dim * 2] = keys.view(np.uint8).reshape(num_pages, -1)
+    qs = ks = None
+    if fmt == "bf16":
+        if page_stride is None:
+            page_stride = PAGE * head_dim * 2
+        q = encode_bf16(rng.standard_normal((rows, head_dim), dtype=np.float32))
+        keys = encode_bf16(rng.standard_normal((num_pages, PAGE, head_dim), dtype=np.float32))
+        key_cache = np.zeros((num_pages, page_stride), dtype=np.uint8)
+        key_cache[:, : PAGE * head_dim * 2] = keys.view(np.uint8).reshape(num_pages, -1)
+    elif fmt == "nvfp4":
+        if page_stride is None:
+            page_stride = PAGE * head_dim // 2
+        if scale_page_stride is None:
+            scale_page_stride = PAGE * head_dim // 16
+        q, qs = quantize_nvfp4(rng.standard_normal((rows, head_dim), dtype=np.float32))
+        kp, kc = quantize_nvfp4(rng.standard_normal((num_pages, PAGE, head_dim),
+                                                    dtype=np.float32))
+        key_cache = np.zeros((num_pages, page_stride), dtype=np.uint8)
+        key_cache[:, : PAGE * head_dim // 2] = kp.reshape(num_pages, -1)
+        ks = np.zeros((num_pages, scale_page_stride), dtype=np.uint8)
+        ks[:, : PAGE * head_dim // 16] = kc.reshape(num_pages, -1)
+    else:
+        raise ValueError(fmt)
     block_table = rng.permutation(num_pages).astype(np.int32).reshape(num_requests, bt_width)
     lengths = rng.integers(0, max_len + 1, size=groups).astype(np.int32)
     reqs = rng.integers(0, num_requests, size=groups).astype(np.int32)
@@ -280,14 +336,16 @@ def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=409
         reqs[zg] = INT32_MAX  # a 0-length group reads nothing; any value is allowed
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     return IndexerInputs(q, key_cache, int(page_stride), block_table, lengths, reqs,
-                         None if uniform_group is not None else offs, int(max_context), name)
+                         None if uniform_group is not None else offs, int(max_context), name,
+                         fmt, qs, ks, int(scale_page_stride or 0))
 
 
 # --------------------------------------------------------------------------
 # named workloads
 # --------------------------------------------------------------------------
 
-SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5}
+SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5,
+         "indexer_nvfp4": 6}
 
 
 def _lens(name, rng):
@@ -302,12 +360,14 @@ def _lens(name, rng):
 
 
 def make_config(name: str, seed: Optional[int] = None, **overrides):
-    """The five named workloads.
+    """The named workloads.
 
     tiny_fp8     B=2, next_n=1, seq_lens {37, 200}, 8 pages, block table a
                  permutation of all 8, fp32 out [2, 256]
     indexer_bf16 24 rows in groups of 1..8 over 6 requests, bf16 keys
                  [384, 64, 128], one zero-length group, fp32 scores [24, 4096]
+    indexer_nvfp4 the same shapes with NVFP4 query and keys (packed e2m1,
+                 e4m3 scale per 16 values)
     decode_fp8   B=64, next_n=1, seq_lens log-uniform in 1K..32K, w ~ N(0, 0.1^2)
     verify_fp8   B=128, next_n=4, seq_lens uniform in 4K..64K, w ~ N(0, 0.1^2)
     mxfp4        B=64, next_n=2, seq_lens uniform in 16K..128K, bf16 out
@@ -317,8 +377,8 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
     if name == "tiny_fp8":
         kw = dict(seq_lens=[37, 200], next_n=1, max_context=256, bt_width=4,
                   full_table=True, w_std=1.0)
-    elif name == "indexer_bf16":
-        kw = dict()
+    elif name in ("indexer_bf16", "indexer_nvfp4"):
+        kw = dict(fmt="bf16" if name == "indexer_bf16" else "nvfp4")
         kw.update(overrides)
         return make_indexer_inputs(seed=seed, name=name, **kw)
     elif name in ("decode_fp8", "verify_fp8", "mxfp4"):

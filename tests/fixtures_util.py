@@ -186,6 +186,43 @@ def indexer_from_case(case):
                                np.array([0, rows], dtype=np.int32), max_context, case["name"])
 
 
+def nvfp4_indexer_from_case(case):
+    """IndexerInputs (fmt nvfp4) from a golden case given as E2M1 / E4M3 codes."""
+    D, P = 128, case["num_pages"]
+    rows = len(case["rows"])
+    qn = np.zeros((rows, D), dtype=np.uint8)
+    qs = np.full((rows, D // 16), 0x38, dtype=np.uint8)
+    for r, row in enumerate(case["rows"]):
+        for d, c in row["q"].items():
+            qn[r, int(d)] = int(c, 16)
+        for b, c in row.get("qs", {}).items():
+            qs[r, int(b)] = int(c, 16)
+    kn = np.zeros((P, 64, D), dtype=np.uint8)
+    ks = np.full((P, 64, D // 16), 0x38, dtype=np.uint8)
+    for tk in case["tokens"]:
+        p = tk["pos"]
+        page, slot = case["block_table"][p // 64], p % 64
+        for d, c in tk["k"].items():
+            kn[page, slot, int(d)] = int(c, 16)
+        for b, c in tk.get("ks", {}).items():
+            ks[page, slot, int(b)] = int(c, 16)
+    pack = lambda n: (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+    L = case["context_length"]
+    max_context = max(64, (L + 63) // 64 * 64)
+    bt = np.array([case["block_table"]], dtype=np.int32)
+    return synth.IndexerInputs(pack(qn), pack(kn).reshape(P, -1).copy(), 64 * D // 2, bt,
+                               np.array([L], dtype=np.int32), np.array([0], dtype=np.int32),
+                               np.array([0, rows], dtype=np.int32), max_context, case["name"],
+                               "nvfp4", qs, ks.reshape(P, -1).copy(), 64 * D // 16)
+
+
+def np_nvfp4(packed, scales):
+    """Dequantised float64 values of NVFP4 data: u8 [..., D/2] packed e2m1 and
+    u8 [..., D/16] e4m3 scales -> float64 [..., D]."""
+    v = np_e2m1_unpack(packed)
+    return v * np.repeat(np_e4m3(scales), 16, axis=-1)
+
+
 # ---------------------------------------------------------------- comparison
 
 

@@ -2,6 +2,7 @@
 library casts for the formats, hand-worked examples, identities of the
 rectifier that reduce the method to a matrix product, scaling invariants and
 the output-contract rules of the pages.  CPU only."""
+import copy
 import math
 
 import numpy as np
@@ -323,3 +324,90 @@ def test_generator_is_deterministic():
     assert np.array_equal(a.kv, b.kv) and np.array_equal(a.q, b.q)
     assert np.array_equal(a.weights, b.weights) and np.array_equal(a.block_table, b.block_table)
     assert sorted(a.block_table.ravel().tolist()) == list(range(8))
+
+
+# ------------------------------------------------------- NVFP4 indexer scores
+
+
+def test_golden_indexer_nvfp4():
+    """Hand-worked NVFP4 cases (codes in, exact values out)."""
+    from fixtures_util import nvfp4_indexer_from_case
+    for case in load_golden("indexer_nvfp4_cases.json")["cases"]:
+        ix = nvfp4_indexer_from_case(case)
+        ref, _, written = oracle.indexer_scores_for(ix)
+        L = case["context_length"]
+        assert written[:, :L].all() and not written[:, L:].any(), case["name"]
+        for r, exp in enumerate(case["expected"]):
+            for col, v in exp.items():
+                assert ref[r, int(col)] == v, (case["name"], r, col, ref[r, int(col)], v)
+
+
+def _nvfp4_small(seed, **kw):
+    kw.setdefault("rows", 12)
+    kw.setdefault("num_requests", 3)
+    kw.setdefault("bt_width", 4)
+    kw.setdefault("max_context", 256)
+    kw.setdefault("max_len", 256)
+    return synth.make_indexer_inputs(seed=seed, fmt="nvfp4", **kw)
+
+
+def test_nvfp4_matches_independent_decode():
+    """float64 matmul of values decoded independently (torch's e4m3 cast, the
+    e2m1 table), gathered through the block table."""
+    from fixtures_util import np_nvfp4
+    ix = _nvfp4_small(21)
+    ref, _, written = oracle.indexer_scores_for(ix)
+    q = np_nvfp4(ix.query, ix.query_scales)
+    P = ix.key_cache.shape[0]
+    keys = np_nvfp4(ix.key_cache[:, :64 * 64].reshape(P, 64, 64),
+                    ix.key_scales[:, :64 * 8].reshape(P, 64, 8))
+    offs = ix.row_offsets()
+    checked = 0
+    for g in range(ix.groups):
+        L = min(max(int(ix.context_lengths[g]), 0), ix.max_context)
+        if L == 0:
+            continue
+        pages = ix.block_table[ix.requests[g]]
+        kmat = np.concatenate([keys[pages[i]] for i in range((L + 63) // 64)])[:L]
+        exp = q[offs[g]:offs[g + 1]] @ kmat.T
+        np.testing.assert_allclose(ref[offs[g]:offs[g + 1], :L], exp, rtol=1e-12, atol=1e-12)
+        checked += exp.size
+    assert checked > 500
+
+
+def test_nvfp4_equals_bf16_indexer_on_dequantised_inputs():
+    """An E2M1 value times an E4M3 scale has at most 6 significant bits, so it
+    is exact in bf16: the NVFP4 path must equal the BF16 path of the oracle
+    on the dequantised tensors, bit for bit."""
+    from fixtures_util import np_nvfp4
+    ix = _nvfp4_small(22)
+    P = ix.key_cache.shape[0]
+    q = np_nvfp4(ix.query, ix.query_scales).astype(np.float32)
+    keys = np_nvfp4(ix.key_cache[:, :4096].reshape(P, 64, 64),
+                    ix.key_scales[:, :512].reshape(P, 64, 8)).astype(np.float32)
+    qb, kb = synth.encode_bf16(q), synth.encode_bf16(keys)
+    from fixtures_util import np_bf16
+    assert np.array_equal(np_bf16(qb), q.astype(np.float64))
+    assert np.array_equal(np_bf16(kb), keys.astype(np.float64))
+    ref_nv, amag_nv, w_nv = oracle.indexer_scores_for(ix)
+    ref_bf, amag_bf, w_bf = oracle.indexer_scores(qb, kb.view(np.uint8).reshape(P, -1), 64 * 256,
+                                                  ix.block_table, ix.context_lengths,
+                                                  ix.requests, ix.row_offsets(), ix.max_context)
+    assert np.array_equal(w_nv, w_bf)
+    assert np.array_equal(ref_nv[w_nv], ref_bf[w_bf])
+    assert np.array_equal(amag_nv[w_nv], amag_bf[w_bf])
+
+
+def test_nvfp4_key_scale_doubling_is_exact():
+    """Raising every key scale's exponent by one doubles every score exactly."""
+    ix = _nvfp4_small(23)
+    ks = ix.key_scales.copy()
+    e = (ks >> 3) & 15
+    assert ((e >= 1) & (e < 14)).all()  # normal scales, no overflow into the NaN code
+    ks = ks + np.uint8(8)
+    ix2 = copy.copy(ix)
+    ix2.key_scales = ks
+    ref, _, w = oracle.indexer_scores_for(ix)
+    ref2, _, w2 = oracle.indexer_scores_for(ix2)
+    assert np.array_equal(w, w2)
+    assert np.array_equal(ref2[w], 2.0 * ref[w])
