@@ -152,6 +152,34 @@ int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void
                    int32_t max_context, void* stream);
 
 /*
+ * indexer_scores_nvfp4 - one-head indexer scores with NVFP4 query and keys.
+ * ("flashinfer.sdsa.indexer_scores": the NVFP4 forms of query and key_cache
+ * and the query_scales / key_scales parameters.)
+ *
+ * A score is the dot product of the dequantised query row and key, where an
+ * NVFP4 value is an e2m1 code (two per byte, the even element in the low
+ * nibble) times the e4m3 scale of its block of 16 values.
+ *
+ *   query            packed e2m1 [rows, 64] (head_dim 128), contiguous, 16-B aligned.
+ *   query_scales     e4m3 [rows, 8], contiguous, 2-B aligned.
+ *   key_cache        packed e2m1 key pages [64, 64]; page i at key_cache +
+ *                    i*page_stride bytes, page_stride >= 4096 and a multiple of 16.
+ *   key_scales       e4m3 [64, 8] per page, paged like the keys: page i's scales at
+ *                    key_scales + i*scale_page_stride bytes, scale_page_stride >= 512
+ *                    and a multiple of 8 (the pages allow any multiple of 8).
+ *   Everything else (block table, lengths, groups, scores, errors) as in
+ *   indexer_scores; head_dim must be 128.
+ */
+int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t rows,
+                         int32_t head_dim, const void* key_cache, int64_t page_stride,
+                         const void* key_scales, int64_t scale_page_stride, int32_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                         int32_t num_requests, const int32_t* context_lengths,
+                         const int32_t* requests, int32_t groups,
+                         const int32_t* group_row_offsets, float* scores,
+                         int64_t scores_row_stride, int32_t max_context, void* stream);
+
+/*
  * mqa_logits_schedule - the per-call work split, computed on the GPU.
  * ("flashinfer.attn_scores", Scheduling and Setup: a per-call work assignment
  * computed on the device, which a caller may build once and pass back.)

@@ -12,7 +12,8 @@ Operations (FlashInfer documentation pages):
     head before the weighted sum, s_p only for FP8, MXFP4 block scales folded
     into q and k; output contract of the page's note.
   * ``indexer_scores`` - "flashinfer.sdsa.indexer_scores": one head, a plain
-    dot product per (query row, key) for groups of 1..8 rows.
+    dot product per (query row, key) for groups of 1..8 rows; BF16 inputs, or
+    NVFP4 inputs with query_scales / key_scales.
   * ``mqa_logits_schedule`` and the helpers - "flashinfer.attn_scores",
     Scheduling and Setup.
 """
@@ -52,6 +53,8 @@ def _load():
                                      I32, I32, P, I64, I32, I32, P, P]
     lib.indexer_scores.argtypes = [P, I32, I32, P, I64, I32, P, I64, I32, I32, P, P, I32, P, P,
                                    I64, I32, P]
+    lib.indexer_scores_nvfp4.argtypes = [P, P, I32, I32, P, I64, P, I64, I32, P, I64, I32, I32,
+                                         P, P, I32, P, P, I64, I32, P]
     lib.mqa_logits_schedule.argtypes = [P, I32, I32, I32, I32, I32, P, P]
     lib.mqa_logits_schedule_ints.argtypes = [I32]
     lib.mqa_logits_schedule_ints.restype = I64
@@ -306,36 +309,52 @@ def prepare_mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, 
 
 
 def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,
-                   group_row_offsets=None, stream=None):
-    """One-head BF16 indexer scores into ``scores`` [rows, max_context] fp32.
+                   query_scales=None, key_scales=None, group_row_offsets=None, stream=None):
+    """One-head indexer scores into ``scores`` [rows, max_context] fp32.
 
-    query [rows, 128] bf16; key_cache [pages, 64, 128] bf16 or [pages, bytes]
-    uint8 (pages may be strided views); block_table [requests, width] int32;
-    context_lengths / requests [groups] int32; group_row_offsets optional
-    [groups+1] int32 (None: rows/groups rows per group)."""
-    args = _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
-                         group_row_offsets, stream)
-    _check(_lib.indexer_scores(*args), "indexer_scores")
+    BF16: query [rows, 128] bf16; key_cache [pages, 64, 128] bf16 or
+    [pages, bytes] uint8 (pages may be strided views).
+    NVFP4 (query_scales and key_scales given): query uint8 [rows, 64] packed
+    e2m1, query_scales e4m3 [rows, 8]; key_cache uint8 [pages, 64, 64] (or
+    [pages, bytes]), key_scales e4m3 [pages, 64, 8] (or [pages, bytes]), each
+    paged by its own first-dimension stride.
+    block_table [requests, width] int32; context_lengths / requests [groups]
+    int32; group_row_offsets optional [groups+1] int32 (None: rows/groups
+    rows per group)."""
+    fn, args, where = _indexer_args(query, key_cache, block_table, context_lengths, requests,
+                                    scores, query_scales, key_scales, group_row_offsets, stream)
+    _check(fn(*args), where)
     return scores
 
 
 def _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
-                  group_row_offsets, stream):
-    rows, D = query.shape
+                  query_scales, key_scales, group_row_offsets, stream):
     bt_stride, bt_width = _rows_of(block_table)
     srs, max_context = _rows_of(scores)
     ps, npages = _pages(key_cache)
-    return (_ptr(query), rows, D, _ptr(key_cache), ps, npages, _ptr(block_table), bt_stride,
-            bt_width, block_table.shape[0], _ptr(context_lengths), _ptr(requests),
-            context_lengths.shape[0], _ptr(group_row_offsets), _ptr(scores), srs, max_context,
-            _stream(stream, query.device))
+    common = (_ptr(block_table), bt_stride, bt_width, block_table.shape[0],
+              _ptr(context_lengths), _ptr(requests), context_lengths.shape[0],
+              _ptr(group_row_offsets), _ptr(scores), srs, max_context,
+              _stream(stream, query.device))
+    if query_scales is None and key_scales is None:
+        rows, D = query.shape
+        return (_lib.indexer_scores, (_ptr(query), rows, D, _ptr(key_cache), ps, npages) + common,
+                "indexer_scores")
+    if query_scales is None or key_scales is None:
+        raise ValueError("NVFP4 inputs need both query_scales and key_scales")
+    rows, half = query.shape
+    sps, _ = _pages(key_scales)
+    return (_lib.indexer_scores_nvfp4,
+            (_ptr(query), _ptr(query_scales), rows, 2 * half, _ptr(key_cache), ps,
+             _ptr(key_scales), sps, npages) + common, "indexer_scores_nvfp4")
 
 
 def prepare_indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,
-                           group_row_offsets=None, stream=None):
+                           query_scales=None, key_scales=None, group_row_offsets=None,
+                           stream=None):
     """indexer_scores with its arguments marshalled once; returns a PreparedCall."""
-    args = _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
-                         group_row_offsets, stream)
-    return PreparedCall(_lib.indexer_scores, args, "indexer_scores", scores,
+    fn, args, where = _indexer_args(query, key_cache, block_table, context_lengths, requests,
+                                    scores, query_scales, key_scales, group_row_offsets, stream)
+    return PreparedCall(fn, args, where, scores,
                         (query, key_cache, block_table, context_lengths, requests,
-                         group_row_offsets))
+                         query_scales, key_scales, group_row_offsets))

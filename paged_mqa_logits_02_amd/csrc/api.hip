@@ -70,7 +70,8 @@ int init_device(int device) {
         }
     hipFuncAttributes attr;
     if (rc == PMQA_OK && (hipFuncGetAttributes(&attr, schedule_kernel_symbol()) != hipSuccess ||
-                          hipFuncGetAttributes(&attr, indexer_kernel_symbol()) != hipSuccess))
+                          hipFuncGetAttributes(&attr, indexer_kernel_symbol()) != hipSuccess ||
+                          hipFuncGetAttributes(&attr, indexer_nvfp4_kernel_symbol()) != hipSuccess))
       rc = PMQA_ERR_HIP;
   }
   if (cur != device && hipSetDevice(cur) != hipSuccess) rc = PMQA_ERR_HIP;
@@ -191,27 +192,31 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
                  out_dtype, schedule, stream);
 }
 
-int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
-                   int64_t page_stride, int32_t num_pages, const int32_t* block_table,
-                   int64_t bt_stride, int32_t bt_width, int32_t num_requests,
-                   const int32_t* context_lengths, const int32_t* requests, int32_t groups,
-                   const int32_t* group_row_offsets, float* scores, int64_t scores_row_stride,
-                   int32_t max_context, void* stream) {
+// Validation shared by both indexer entry points; key_bytes is the packed size
+// of one page of keys.  Returns PMQA_OK with *launch = false when there is
+// nothing to do.
+static int check_indexer(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
+                  int64_t page_stride, int64_t key_bytes, int32_t num_pages,
+                  const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                  int32_t num_requests, const int32_t* context_lengths, const int32_t* requests,
+                  int32_t groups, const int32_t* group_row_offsets, float* scores,
+                  int64_t scores_row_stride, int32_t max_context, int* uniform_g, bool* launch) {
+  *launch = false;
   if (rows < 0 || groups < 0 || groups > 65535 || head_dim < 1) return PMQA_ERR_SHAPE;
   if (head_dim != 128) return PMQA_ERR_UNSUPPORTED;
   if (max_context < 0 || max_context % PMQA_PAGE_TOKENS != 0) return PMQA_ERR_SHAPE;
   if (groups > 0 && rows < 1) return PMQA_ERR_SHAPE;
-  int uniform_g = 0;
+  *uniform_g = 0;
   if (!group_row_offsets && groups > 0) {
     if (rows % groups != 0) return PMQA_ERR_SHAPE;
-    uniform_g = rows / groups;
-    if (uniform_g < 1 || uniform_g > 8) return PMQA_ERR_SHAPE;
+    *uniform_g = rows / groups;
+    if (*uniform_g < 1 || *uniform_g > 8) return PMQA_ERR_SHAPE;
   }
   if (groups == 0 || max_context == 0) return PMQA_OK;
   if (!query || !key_cache || !block_table || !context_lengths || !requests || !scores)
     return PMQA_ERR_NULL;
   if (num_pages < 1 || num_requests < 1) return PMQA_ERR_SHAPE;
-  if (page_stride < (int64_t)PMQA_PAGE_TOKENS * head_dim * 2) return PMQA_ERR_SHAPE;
+  if (page_stride < key_bytes) return PMQA_ERR_SHAPE;
   if (page_stride % 16 != 0) return PMQA_ERR_ALIGN;
   if (bt_width < 1 || bt_stride < bt_width) return PMQA_ERR_SHAPE;
   if ((int64_t)bt_width * PMQA_PAGE_TOKENS < max_context) return PMQA_ERR_SHAPE;
@@ -221,13 +226,34 @@ int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void
        reinterpret_cast<uintptr_t>(context_lengths) | reinterpret_cast<uintptr_t>(requests) |
        reinterpret_cast<uintptr_t>(group_row_offsets)) & 3)
     return PMQA_ERR_ALIGN;
+  *launch = true;
+  return PMQA_OK;
+}
+
+int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
+                   int64_t page_stride, int32_t num_pages, const int32_t* block_table,
+                   int64_t bt_stride, int32_t bt_width, int32_t num_requests,
+                   const int32_t* context_lengths, const int32_t* requests, int32_t groups,
+                   const int32_t* group_row_offsets, float* scores, int64_t scores_row_stride,
+                   int32_t max_context, void* stream) {
+  int uniform_g = 0;
+  bool launch = false;
+  int rc = check_indexer(query, rows, head_dim, key_cache, page_stride,
+                         (int64_t)PMQA_PAGE_TOKENS * 128 * 2, num_pages, block_table, bt_stride,
+                         bt_width, num_requests, context_lengths, requests, groups,
+                         group_row_offsets, scores, scores_row_stride, max_context, &uniform_g,
+                         &launch);
+  if (rc != PMQA_OK || !launch) return rc;
   DeviceInfo* d = nullptr;
-  int rc = current_device_info(&d);
+  rc = current_device_info(&d);
   if (rc != PMQA_OK) return rc;
   IdxArgs a;
   a.q = static_cast<const uint16_t*>(query);
   a.kc = static_cast<const uint8_t*>(key_cache);
   a.page_stride = page_stride;
+  a.qs = nullptr;
+  a.ks = nullptr;
+  a.scale_page_stride = 0;
   a.bt = block_table;
   a.bt_stride = bt_stride;
   a.lens = context_lengths;
@@ -242,6 +268,55 @@ int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void
   a.uniform_g = uniform_g;
   a.max_context = max_context;
   if (launch_indexer(a, static_cast<hipStream_t>(stream)) != hipSuccess) return PMQA_ERR_HIP;
+  return PMQA_OK;
+}
+
+int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t rows,
+                         int32_t head_dim, const void* key_cache, int64_t page_stride,
+                         const void* key_scales, int64_t scale_page_stride, int32_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                         int32_t num_requests, const int32_t* context_lengths,
+                         const int32_t* requests, int32_t groups,
+                         const int32_t* group_row_offsets, float* scores,
+                         int64_t scores_row_stride, int32_t max_context, void* stream) {
+  int uniform_g = 0;
+  bool launch = false;
+  int rc = check_indexer(query, rows, head_dim, key_cache, page_stride,
+                         (int64_t)PMQA_PAGE_TOKENS * 128 / 2, num_pages, block_table, bt_stride,
+                         bt_width, num_requests, context_lengths, requests, groups,
+                         group_row_offsets, scores, scores_row_stride, max_context, &uniform_g,
+                         &launch);
+  if (rc != PMQA_OK || !launch) return rc;
+  if (!query_scales || !key_scales) return PMQA_ERR_NULL;
+  if (scale_page_stride < (int64_t)PMQA_PAGE_TOKENS * 8) return PMQA_ERR_SHAPE;
+  if (scale_page_stride % 8 != 0) return PMQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(query_scales) | reinterpret_cast<uintptr_t>(key_scales)) & 1)
+    return PMQA_ERR_ALIGN;
+  DeviceInfo* d = nullptr;
+  rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
+  IdxArgs a;
+  a.q = static_cast<const uint16_t*>(query);
+  a.kc = static_cast<const uint8_t*>(key_cache);
+  a.page_stride = page_stride;
+  a.qs = static_cast<const uint8_t*>(query_scales);
+  a.ks = static_cast<const uint8_t*>(key_scales);
+  a.scale_page_stride = scale_page_stride;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.lens = context_lengths;
+  a.reqs = requests;
+  a.offs = group_row_offsets;
+  a.scores = scores;
+  a.srs = scores_row_stride;
+  a.num_pages = num_pages;
+  a.num_requests = num_requests;
+  a.rows = rows;
+  a.groups = groups;
+  a.uniform_g = uniform_g;
+  a.max_context = max_context;
+  if (launch_indexer_nvfp4(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PMQA_ERR_HIP;
   return PMQA_OK;
 }
 

@@ -1,4 +1,4 @@
-// One-head BF16 indexer scores on gfx950.
+// One-head indexer scores on gfx950 (BF16 and NVFP4 inputs).
 //
 // scores[r, k] = query[r] . key_k for every query row r of group g and every
 // key k below the group's length, keys gathered through the group's
@@ -70,6 +70,124 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
       if (row < G && col < L) a.scores[(long long)(r0 + row) * a.srs + col] = bad ? nan : acc[s][i];
     }
   }
+}
+
+// ------------------------------------------------------------------ NVFP4
+//
+// The same contraction with NVFP4 query rows and keys: packed e2m1, an e4m3
+// scale per 16 values (query_scales [rows, 8]; key_scales [pages, 64, 8],
+// paged like the keys).  An e2m1 value times an e4m3 scale has at most six
+// significant bits, so each side is dequantised exactly into bf16 registers and
+// the bf16 MFMA computes the products exactly, accumulating in fp32.
+//
+// K mapping: lane (kg = l>>4) holds, in K step ks, head_dim values
+// 32kg + 8ks .. 32kg + 8ks + 7, the same for query and key, so the four K
+// steps of a lane are one contiguous 16-byte slice of a packed row and two of
+// its scales (blocks 2kg and 2kg+1).
+
+// Eight dequantised values (one packed dword, scale s) as bf16.
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two e2m1 values of byte B of `packed` (low nibble first) times s, as bf16;
+// exact (the conversion applies only a power-of-two scale, so s is applied
+// by a separate fp32 multiply).
+template <int B>
+__device__ __forceinline__ void dequant2(uint32_t packed, float s, v8bf& r) {
+  const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, B);
+  r[2 * B] = (__bf16)(f[0] * s);
+  r[2 * B + 1] = (__bf16)(f[1] * s);
+}
+
+__device__ __forceinline__ v8bf dequant8(uint32_t packed, float s) {
+  v8bf r;
+  dequant2<0>(packed, s, r);
+  dequant2<1>(packed, s, r);
+  dequant2<2>(packed, s, r);
+  dequant2<3>(packed, s, r);
+  return r;
+}
+
+// A lane's 32 values of one NVFP4 row (16 packed bytes, two e4m3 scales) as
+// the four K-step fragments.
+__device__ __forceinline__ void dequant_row(const v4i& packed, uint32_t scales2, v8bf out[4]) {
+  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)scales2, 0);
+  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)scales2, 1);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) out[ks] = dequant8((uint32_t)packed[ks], ks < 2 ? s0 : s1);
+}
+
+__global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
+  const int g = blockIdx.y;
+  const int pi = blockIdx.x;
+  const int lane = threadIdx.x;
+  int L = a.lens[g];
+  L = L < a.max_context ? L : a.max_context;
+  if (L <= pi * kPage) return;  // also every group of length <= 0
+
+  int r0, G;
+  if (a.offs) {
+    r0 = a.offs[g];
+    G = a.offs[g + 1] - r0;
+  } else {
+    r0 = g * a.uniform_g;
+    G = a.uniform_g;
+  }
+  if (G < 1 || G > 8 || r0 < 0 || r0 + G > a.rows) return;
+
+  const int req = a.reqs[g];
+  bool bad = (unsigned)req >= (unsigned)a.num_requests;
+  int pg = bad ? 0 : a.bt[(long long)req * a.bt_stride + pi];
+  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
+
+  const int kg = lane >> 4, r = lane & 15;
+  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
+  v8bf qa[4];
+  if (r < G) {
+    const long long row = r0 + r;
+    const v4i packed = ldg<v4i>(q8 + row * 64 + 16 * kg);
+    const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.qs + row * 8 + 2 * kg);
+    dequant_row(packed, sc, qa);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8bf){};
+  }
+
+  const uint8_t* page = a.kc + (long long)pg * a.page_stride;
+  const uint8_t* pscale = a.ks + (long long)pg * a.scale_page_stride;
+  v4f acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (!bad) {
+      const int key = 16 * s + r;
+      const v4i packed = ldg_stream<v4i>(page + key * 64 + 16 * kg);
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
+      v8bf kb[4];
+      dequant_row(packed, sc, kb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
+    }
+  }
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int col = pi * kPage + 16 * s + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kg + i;
+      if (row < G && col < L) a.scores[(long long)(r0 + row) * a.srs + col] = bad ? nan : acc[s][i];
+    }
+  }
+}
+
+hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream) {
+  dim3 grid(a.max_context / kPage, a.groups);
+  hipLaunchKernelGGL(indexer_nvfp4_kernel, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+const void* indexer_nvfp4_kernel_symbol() {
+  return reinterpret_cast<const void*>(&indexer_nvfp4_kernel);
 }
 
 hipError_t launch_indexer(const IdxArgs& a, hipStream_t stream) {

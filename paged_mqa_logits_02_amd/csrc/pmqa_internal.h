@@ -31,9 +31,12 @@ struct MqaArgs {
 };
 
 struct IdxArgs {
-  const uint16_t* q;        // bf16 [rows, 128]
-  const uint8_t* kc;        // pages of bf16 [64, 128]
+  const uint16_t* q;        // bf16 [rows, 128]; NVFP4: packed e2m1 [rows, 64]
+  const uint8_t* kc;        // pages of bf16 [64, 128]; NVFP4: packed e2m1 [64, 64]
   long long page_stride;
+  const uint8_t* qs;        // NVFP4 only: e4m3 [rows, 8]
+  const uint8_t* ks;        // NVFP4 only: pages of e4m3 [64, 8]
+  long long scale_page_stride;
   const int32_t* bt;        // [num_requests, bt_stride]
   long long bt_stride;
   const int32_t* lens;      // [groups]
@@ -53,11 +56,13 @@ const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype);
 size_t mqa_ring_bytes(int variant);  // LDS of the page ring (before the request prefix)
 const void* schedule_kernel_symbol();
 const void* indexer_kernel_symbol();
+const void* indexer_nvfp4_kernel_symbol();
 
 hipError_t launch_mqa(const MqaArgs& a, int next_n, int variant, int out_dtype, int grid,
                       size_t lds_bytes, hipStream_t stream);
 hipError_t launch_schedule(const int32_t* seq_lens, int B, int next_n, int variant,
                            int max_context, int U, int32_t* sched, hipStream_t stream);
 hipError_t launch_indexer(const IdxArgs& a, hipStream_t stream);
+hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream);
 
 }  // namespace pmqa

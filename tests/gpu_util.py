@@ -142,10 +142,18 @@ def check_sampled(dm, out, rng, what=""):
 
 
 class DevIndexer:
-    def __init__(self, ix, key_cache=None):
+    """Device copies of a synth.IndexerInputs (BF16 or NVFP4)."""
+
+    def __init__(self, ix, key_cache=None, key_scales=None):
         self.ix = ix
         t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-        self.q = t(ix.query.view(np.int16)).view(torch.bfloat16)
+        if getattr(ix, "fmt", "bf16") == "nvfp4":
+            self.q = t(ix.query)
+            self.qs = t(ix.query_scales)
+            self.ks = t(ix.key_scales) if key_scales is None else key_scales
+        else:
+            self.q = t(ix.query.view(np.int16)).view(torch.bfloat16)
+            self.qs = self.ks = None
         self.kc = t(ix.key_cache) if key_cache is None else key_cache
         self.bt = t(ix.block_table)
         self.lens = t(ix.context_lengths)
@@ -156,7 +164,8 @@ class DevIndexer:
         scores = torch.empty((self.ix.rows, self.ix.max_context), dtype=torch.float32, device=DEV)
         scores.view(torch.int32).fill_(F32_SENTINEL)
         pm().indexer_scores(self.q, self.kc, self.bt, self.lens, requests=self.reqs,
-                            scores=scores, group_row_offsets=self.offs)
+                            scores=scores, query_scales=self.qs, key_scales=self.ks,
+                            group_row_offsets=self.offs)
         return scores
 
 

@@ -33,7 +33,8 @@ def pm():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mqa_logits_fp8", "mqa_logits_mxfp4", "indexer_scores", "mqa_logits_schedule",
+    for n in ("mqa_logits_fp8", "mqa_logits_mxfp4", "indexer_scores", "indexer_scores_nvfp4",
+              "mqa_logits_schedule",
               "mqa_logits_schedule_ints", "mqa_logits_num_units", "mqa_logits_padded_seq_len",
               "mqa_logits_min_block_table_width", "mqa_logits_init", "mqa_logits_status_string"):
         assert n in names, n
@@ -126,6 +127,28 @@ def _idx(lib, **kw):
 ])
 def test_indexer_validation(pm, kw, rc):
     assert _idx(pm.library(), **kw) == rc
+
+
+def _idx4(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, rows=24, D=128, kc=FAKE, ps=4096, ks=FAKE, sps=512, npages=384,
+             bt=FAKE, bts=64, btw=64, nreq=6, lens=FAKE, reqs=FAKE, groups=6, offs=None,
+             scores=FAKE, srs=4096, maxc=4096, stream=None)
+    a.update(kw)
+    return lib.indexer_scores_nvfp4(a["q"], a["qs"], a["rows"], a["D"], a["kc"], a["ps"],
+                                    a["ks"], a["sps"], a["npages"], a["bt"], a["bts"], a["btw"],
+                                    a["nreq"], a["lens"], a["reqs"], a["groups"], a["offs"],
+                                    a["scores"], a["srs"], a["maxc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(D=64), UNSUP), (dict(groups=5), SHAPE), (dict(ps=4096 - 16), SHAPE),
+    (dict(ps=4096 + 8), ALIGN), (dict(sps=504), SHAPE), (dict(sps=516), ALIGN),
+    (dict(qs=None), NULL), (dict(ks=None), NULL), (dict(q=None), NULL),
+    (dict(qs=FAKE + 1), ALIGN), (dict(q=FAKE + 8), ALIGN), (dict(btw=32), SHAPE),
+    (dict(groups=0), OK),
+])
+def test_indexer_nvfp4_validation(pm, kw, rc):
+    assert _idx4(pm.library(), **kw) == rc
 
 
 def test_schedule_validation(pm):

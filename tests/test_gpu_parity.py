@@ -168,6 +168,69 @@ def test_indexer_strided_pages():
     assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
 
 
+# ------------------------------------------------------ NVFP4 indexer
+
+
+@pytest.mark.parametrize("case", load_golden("indexer_nvfp4_cases.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_indexer_nvfp4_golden_bit_exact(case):
+    from fixtures_util import nvfp4_indexer_from_case
+    di = DevIndexer(nvfp4_indexer_from_case(case))
+    got, wrote = host_out(di.run())
+    L = case["context_length"]
+    assert wrote[:, :L].all() and not wrote[:, L:].any()
+    for r, exp in enumerate(case["expected"]):
+        for col, v in exp.items():
+            if int(col) < L:
+                assert got[r, int(col)] == v
+
+
+@pytest.mark.parametrize("uniform", [None, 4, 1, 8])
+def test_indexer_nvfp4_config(uniform):
+    ix = synth.make_config("indexer_nvfp4", uniform_group=uniform)
+    say("nvfp4 indexer groups=%d uniform=%s" % (ix.groups, uniform))
+    di = DevIndexer(ix)
+    check_indexer(di, di.run(), "nvfp4 indexer uniform=%s" % uniform)
+
+
+def test_indexer_nvfp4_fused_pages():
+    """Keys and scales as two views of one cache holding each page's keys and
+    then their scales (page stride a multiple of 16, not of the key size):
+    bit-identical to separate buffers."""
+    ix = synth.make_config("indexer_nvfp4")
+    P = ix.key_cache.shape[0]
+    stride = 4096 + 512 + 16 * 3
+    fused = np.zeros((P, stride), dtype=np.uint8)
+    fused[:, :4096] = ix.key_cache[:, :4096]
+    fused[:, 4096:4608] = ix.key_scales[:, :512]
+    dev = torch.from_numpy(fused).to(DEV)
+    a, _ = host_out(DevIndexer(ix).run())
+    b, _ = host_out(DevIndexer(ix, key_cache=dev[:, :4096], key_scales=dev[:, 4096:4608]).run())
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_indexer_nvfp4_out_of_range_page_is_nan():
+    ix = synth.make_config("indexer_nvfp4")
+    g = int(np.argmax(ix.context_lengths))
+    bad = copy.copy(ix)
+    bad.block_table = ix.block_table.copy()
+    bad.block_table[ix.requests[g], 0] = ix.key_cache.shape[0] + 3
+    got, wrote = host_out(DevIndexer(bad).run())
+    ref, amag, written = oracle.indexer_scores_for(ix)
+    assert np.array_equal(wrote, written)
+    poison = np.zeros_like(written)
+    poison[:, :64] = True
+    rows_of = np.zeros(ix.rows, dtype=bool)
+    offs = ix.row_offsets()
+    for h in range(ix.groups):
+        if ix.requests[h] == ix.requests[g] and ix.context_lengths[h] > 0:
+            rows_of[offs[h]:offs[h + 1]] = True
+    poison &= rows_of[:, None] & written
+    assert poison.any() and np.isnan(got[poison]).all()
+    ok = written & ~poison
+    check_values(got[ok], ref[ok], np.abs(ref[ok]) + 0 * amag[ok], (2e-3, 1e-5), "valid pages")
+
+
 # ------------------------------------------------------- full-size configs
 
 
