@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV positions/sec and achieved HBM GB/s, fp8 paged MQA logits H=64 d=128"
 METRIC_MXFP4 = "KV positions/sec and achieved HBM GB/s, mxfp4 paged MQA logits H=64 d=128"
 METRIC_INDEXER = "KV positions/sec and achieved HBM GB/s, one-head bf16 indexer scores d=128"
+METRIC_INDEXER_NVFP4 = ("KV positions/sec and achieved HBM GB/s, one-head nvfp4 indexer scores "
+                        "d=128")
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -43,6 +45,8 @@ WORKLOADS = {
     "mxfp4": "B=64, next_n=2, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
     "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
+    "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "
+                     "16 values, key scales paged like the keys)",
 }
 
 
@@ -149,12 +153,19 @@ def copy_calibration(steps):
 
 
 def run_indexer(args, torch, synth, pm, dev):
-    """The one-head BF16 indexer workload: one indexer_scores call per step."""
-    inp = synth.make_config("indexer_bf16")
-    key_bytes = inp.key_cache.nbytes
+    """The one-head indexer workloads: one indexer_scores call per step."""
+    nvfp4 = args.workload == "indexer_nvfp4"
+    inp = synth.make_config(args.workload)
+    key_bytes = inp.key_cache.nbytes + (inp.key_scales.nbytes if nvfp4 else 0)
     R = args.replicas or max(2, -(-2 * MALL_BYTES // key_bytes))
     keys = [torch.from_numpy(inp.key_cache).to(dev) for _ in range(R)]
-    qry = torch.from_numpy(inp.query.view(np.int16)).to(dev).view(torch.bfloat16)
+    kscales = [torch.from_numpy(inp.key_scales).to(dev) for _ in range(R)] if nvfp4 else [None]
+    if nvfp4:
+        qry = torch.from_numpy(inp.query).to(dev)
+        qsc = torch.from_numpy(inp.query_scales).to(dev)
+    else:
+        qry = torch.from_numpy(inp.query.view(np.int16)).to(dev).view(torch.bfloat16)
+        qsc = None
     bt = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.context_lengths).to(dev)
     reqs = torch.from_numpy(inp.requests).to(dev)
@@ -165,8 +176,10 @@ def run_indexer(args, torch, synth, pm, dev):
     import math
     L = R * 2 // math.gcd(R, 2)
     calls = [pm.prepare_indexer_scores(qry, keys[i % R], bt, lens, requests=reqs,
-                                       scores=scores[i % 2], group_row_offsets=offs,
-                                       stream=stream) for i in range(L)]
+                                       scores=scores[i % 2], query_scales=qsc,
+                                       key_scales=kscales[i % R] if nvfp4 else None,
+                                       group_row_offsets=offs, stream=stream)
+             for i in range(L)]
     t_ramp = time.time() + args.ramp
     i = 0
     while time.time() < t_ramp:
@@ -189,16 +202,19 @@ def run_indexer(args, torch, synth, pm, dev):
     kern = total_ms / K
     lens_np = np.minimum(np.maximum(inp.context_lengths, 0), inp.max_context).astype(np.int64)
     sizes = np.diff(inp.row_offsets()).astype(np.int64)
-    alg = int((lens_np * (256 + 4 * sizes)).sum())  # key bytes + one score per row, per key
+    # per key and group: its packed values (and scales) + one fp32 score per row
+    key_b = 64 + 8 if nvfp4 else 256
+    alg = int((lens_np * (key_b + 4 * sizes)).sum())
     positions = int(lens_np.sum())
     achieved = alg / (kern * 1e-3) / 1e9
     line = {
-        "metric": METRIC_INDEXER, "value": positions * K / (total_ms * 1e-3),
+        "metric": METRIC_INDEXER_NVFP4 if nvfp4 else METRIC_INDEXER,
+        "value": positions * K / (total_ms * 1e-3),
         "unit": "KV positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": kern, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "nvfp4" if nvfp4 else "bf16", "data": "synthetic",
         "gb_per_s": achieved,
-        "config": {"workload": "indexer_bf16", "shape": WORKLOADS["indexer_bf16"],
+        "config": {"workload": args.workload, "shape": WORKLOADS[args.workload],
                    "rows": inp.rows, "groups": inp.groups, "max_context": inp.max_context,
                    "kv_positions": positions, "key_replicas": R, "kernel_ms_avg": kern,
                    "timing": "host launches of prepared calls, events around the %d launches" % K,
@@ -246,7 +262,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pm.init(0)
-    if args.workload == "indexer_bf16":
+    if args.workload.startswith("indexer_"):
         run_indexer(args, torch, synth, pm, dev)
         return
     inp = synth.make_config(args.workload)
