@@ -260,6 +260,63 @@ def test_mxfp4_group_scale_changes_result_non_proportionally():
     assert np.ptp(ratio) > 1e-3  # not one common factor
 
 
+# ------------------------------------------- other head counts, dims, next_n
+
+# (num_heads, head_dim, next_n): head counts that are not multiples of 16 or
+# 32, head_dims that are not multiples of 128, and next_n above 4
+OTHER_SHAPES = [(1, 16, 1), (3, 32, 5), (5, 48, 6), (33, 144, 3), (128, 256, 2), (64, 128, 8),
+                (64, 128, 5)]
+
+
+def _brute_force(inp):
+    """The equation cell by cell in plain Python over independently decoded
+    data: s_p * sum_h w[r,h] * max(0, sum_d q[b,t,h,d] k_p[d])."""
+    Q = decode_queries(inp).tolist()
+    W = inp.weights.astype(np.float64).tolist()
+    out = {}
+    for b, (k, s) in enumerate(decode_keys(inp)):
+        kl = k.tolist()
+        for t in range(inp.next_n):
+            r = b * inp.next_n + t
+            for p in range(len(kl)):
+                acc = 0.0
+                for h in range(inp.num_heads):
+                    dot = 0.0
+                    for d in range(inp.head_dim):
+                        dot += Q[b][t][h][d] * kl[p][d]
+                    acc += W[r][h] * max(dot, 0.0)
+                out[r, p] = float(s[p]) * acc
+    return out
+
+
+@pytest.mark.parametrize("H,D,N", [(3, 32, 5), (1, 16, 2), (5, 48, 1), (2, 144, 7)])
+def test_brute_force_at_other_shapes(H, D, N):
+    inp = synth.make_mqa_inputs([70, 0, 5], N, num_heads=H, head_dim=D, max_context=128,
+                                bt_width=2, seed=30 + H + D, w_std=1.0)
+    ref, amag, m = oracle.mqa_logits_for(inp)
+    bf = _brute_force(inp)
+    assert int(m.sum()) == len(bf)
+    for (r, p), v in bf.items():
+        assert m[r, p]
+        assert abs(ref[r, p] - v) <= 1e-12 * amag[r, p] + 1e-300, (r, p)
+
+
+@pytest.mark.parametrize("H,D,N", OTHER_SHAPES)
+def test_rectifier_identities_at_other_shapes(H, D, N):
+    """The difference and sum identities of the rectifier (see above) at head
+    counts, head_dims and next_n other than 64, 128 and 1..4."""
+    inp = synth.make_mqa_inputs([37, 0, 130, 64], N, num_heads=H, head_dim=D, max_context=192,
+                                bt_width=3, seed=40 + N, w_std=1.0)
+    r1, a1, m = oracle.mqa_logits_for(inp)
+    r2, _, m2 = oracle.mqa_logits_for(flip_key_signs(inp))
+    assert np.array_equal(m, m2)
+    lin = _weighted_query_dot(inp, "lin")
+    ab = _weighted_query_dot(inp, "abs")
+    np.testing.assert_allclose((r1 - r2)[m], lin[m], rtol=1e-12, atol=1e-9 * np.max(a1))
+    np.testing.assert_allclose((r1 + r2)[m], ab[m], rtol=1e-12, atol=1e-9 * np.max(a1))
+    assert np.array_equal(np.isnan(lin), ~m)
+
+
 # ------------------------------------------------------------------ indexer
 
 
