@@ -55,7 +55,7 @@ enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_MXFP4 = 1 };
 
 #define PMQA_PAGE_TOKENS 64
 #define PMQA_MAX_BATCH 8192  /* requests per call                       */
-#define PMQA_MAX_NEXT_N 4    /* query tokens per request (next_n)       */
+#define PMQA_MAX_NEXT_N 8    /* query tokens per request (next_n)       */
 
 /*
  * mqa_logits_fp8 - FP8 paged MQA logits.
@@ -82,13 +82,23 @@ enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_MXFP4 = 1 };
  *                meaningful; masking beyond that is the caller's job.
  *                max_context % 64 == 0, out_row_stride >= max_context.
  *   acc_dtype    PMQA_F32 (the only accumulator; anything else -> UNSUPPORTED).
+ *                With 64 heads and head_dim 128 the products are FP8 matrix
+ *                products, whose sums keep each product only down to 2^-13 of
+ *                the largest product of a 128-value block; other shapes widen
+ *                the operands exactly to f16 and sum at fp32 precision.
  *   schedule     NULL (the kernel splits the work itself, on the GPU) or a buffer
  *                filled by mqa_logits_schedule() with the same next_n, variant
  *                and max_context, valid only while seq_lens is unchanged
  *                ("flashinfer.attn_scores", Scheduling and Setup, and its warning).
  *                A schedule built for other arguments is detected on the device
  *                and ignored.
- *   Supported: num_heads == 64, head_dim == 128, 1 <= next_n <= 4.
+ *   Supported (the FP8 variant's shapes are parametric: "flashinfer.attn_scores",
+ *   paragraph on how the variants differ): 1 <= num_heads <= 128,
+ *   head_dim a multiple of 16 in 16..256, 1 <= next_n <= 8; other values ->
+ *   UNSUPPORTED.  A call is one or more kernel launches on `stream`, each over
+ *   a group of query slots (up to 4 with 64 heads x 128; otherwise as many as
+ *   fit a 32 KB query slice of the padded heads).  q and weights are read
+ *   once per launch; the pages once per launch.
  */
 int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int32_t num_pages,
                    const float* weights, const int32_t* seq_lens, const int32_t* block_table,
@@ -112,6 +122,8 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
  *                multiple of 16.
  *   out_dtype    PMQA_BF16 (the default of this variant, round to nearest even)
  *                or PMQA_F32.
+ *   Supported: num_heads == 64, head_dim == 128 (other values -> UNSUPPORTED),
+ *   1 <= next_n <= 8 (next_n above 4 runs as two launches over the slots).
  *   Everything else as in mqa_logits_fp8.
  */
 int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,

@@ -224,9 +224,10 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                    output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
     """FP8 paged MQA logits; returns ``out`` [batch*next_n, max_context].
 
-    q [batch, next_n, 64, 128] e4m3 (uint8 or float8_e4m3fn); kv_fused
+    q [batch, next_n, heads, head_dim] e4m3 (uint8 or float8_e4m3fn; heads
+    1..128, head_dim a multiple of 16 up to 256, next_n 1..8); kv_fused
     [pages, page_bytes] uint8 (a strided view is fine); weights
-    [batch*next_n, 64] fp32; seq_lens [batch] int32; block_table
+    [batch*next_n, heads] fp32; seq_lens [batch] int32; block_table
     [batch, width] int32.  Columns at or beyond ceil(seq_len/64)*64 and rows
     of empty requests are not written (out=None allocates uninitialised
     memory)."""

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpmqa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "mqa_logits.hip", "indexer.hip"]
+SOURCES = ["api.hip", "mqa_logits.hip", "mqa_any.hip", "indexer.hip"]
 ARCH = "gfx950"
 
 
@@ -31,7 +31,8 @@ def hipcc() -> str:
 # Per-source extras.  The logits kernels: MFMA results in VGPRs (no copies out
 # of accumulation registers), and no NaN semantics for arithmetic so the
 # rectifier is one v_max_f32 (NaN outputs are written as bit patterns there).
-EXTRA_FLAGS = {"mqa_logits.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_LOGITS_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"mqa_logits.hip": _LOGITS_FLAGS, "mqa_any.hip": _LOGITS_FLAGS}
 
 
 def compile_flags(src=None):

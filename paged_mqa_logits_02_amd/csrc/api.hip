@@ -15,23 +15,47 @@ struct DeviceInfo {
   bool ready = false;
   int cus = 0;
   size_t lds_per_cu = 0;
-  // workgroups per CU for each kernel instance [next_n-1][variant][out],
-  // from registers alone, and each instance's static LDS bytes
-  int occ[PMQA_MAX_NEXT_N][2][2] = {};
-  size_t static_lds[PMQA_MAX_NEXT_N][2][2] = {};
+  // workgroups per CU of each 64-head kernel instance [slots-1][variant][out]
+  // and of each general FP8 instance [ks-1][out], from registers alone, and
+  // each instance's static LDS bytes
+  int occ[kFastSlots][2][2] = {};
+  size_t static_lds[kFastSlots][2][2] = {};
+  int occ_any[2][2] = {};
+  size_t static_lds_any[2][2] = {};
 };
 
-// Resident workgroups per CU of a logits kernel instance launched with
-// `dyn_lds` bytes of dynamic LDS: the register limit, further limited by LDS
-// (dynamic plus static, in whole 1 KiB allocation blocks).
-int blocks_per_cu(const DeviceInfo& d, int next_n, int variant, int out, size_t dyn_lds) {
-  int occ = d.occ[next_n - 1][variant][out];
+// Resident workgroups per CU of a kernel whose register limit is `occ`,
+// launched with `dyn_lds` bytes of dynamic LDS and `static_lds` of static LDS
+// (in whole 1 KiB allocation blocks).
+int limit_by_lds(const DeviceInfo& d, int occ, size_t static_lds, size_t dyn_lds) {
   if (d.lds_per_cu > 0) {
-    const size_t per_block = (dyn_lds + d.static_lds[next_n - 1][variant][out] + 1023) / 1024 * 1024;
+    const size_t per_block = (dyn_lds + static_lds + 1023) / 1024 * 1024;
     const int by_lds = (int)(d.lds_per_cu / per_block);
     if (by_lds >= 1 && by_lds < occ) occ = by_lds;
   }
   return occ;
+}
+
+int blocks_per_cu(const DeviceInfo& d, int slots, int variant, int out, size_t dyn_lds) {
+  return limit_by_lds(d, d.occ[slots - 1][variant][out], d.static_lds[slots - 1][variant][out],
+                      dyn_lds);
+}
+
+int blocks_per_cu_any(const DeviceInfo& d, int ks, int out, size_t dyn_lds) {
+  return limit_by_lds(d, d.occ_any[ks - 1][out], d.static_lds_any[ks - 1][out], dyn_lds);
+}
+
+// Register-limited occupancy and static LDS of one kernel; also loads its
+// code object.
+bool query_kernel(const void* fn, int* occ, size_t* static_lds) {
+  int blocks = 0;
+  hipFuncAttributes attr;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kBlockThreads, 0) != hipSuccess ||
+      hipFuncGetAttributes(&attr, fn) != hipSuccess)
+    return false;
+  *occ = blocks > 0 ? blocks : 1;
+  *static_lds = attr.sharedSizeBytes;
+  return true;
 }
 
 std::mutex g_mu;
@@ -52,22 +76,19 @@ int init_device(int device) {
   } else {
     d.cus = prop.multiProcessorCount;
     d.lds_per_cu = prop.maxSharedMemoryPerMultiProcessor;
-    for (int n = 1; n <= PMQA_MAX_NEXT_N && rc == PMQA_OK; ++n)
+    // occupancy from registers (LDS is accounted per call: it depends on
+    // the batch and the shape)
+    for (int n = 1; n <= kFastSlots && rc == PMQA_OK; ++n)
       for (int v = 0; v < 2 && rc == PMQA_OK; ++v)
-        for (int o = 0; o < 2 && rc == PMQA_OK; ++o) {
-          int blocks = 0;
-          hipFuncAttributes attr;
-          // Occupancy from registers (LDS is accounted per call, it depends
-          // on the batch); also loads the code object.
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mqa_kernel_symbol(n, v, o),
-                                                           kBlockThreads, 0) != hipSuccess ||
-              hipFuncGetAttributes(&attr, mqa_kernel_symbol(n, v, o)) != hipSuccess) {
+        for (int o = 0; o < 2 && rc == PMQA_OK; ++o)
+          if (!query_kernel(mqa_kernel_symbol(n, v, o), &d.occ[n - 1][v][o],
+                            &d.static_lds[n - 1][v][o]))
             rc = PMQA_ERR_HIP;
-          } else {
-            d.occ[n - 1][v][o] = blocks > 0 ? blocks : 1;
-            d.static_lds[n - 1][v][o] = attr.sharedSizeBytes;
-          }
-        }
+    for (int ks = 1; ks <= 2 && rc == PMQA_OK; ++ks)
+      for (int o = 0; o < 2 && rc == PMQA_OK; ++o)
+        if (!query_kernel(mqa_any_kernel_symbol(ks, o), &d.occ_any[ks - 1][o],
+                          &d.static_lds_any[ks - 1][o]))
+          rc = PMQA_ERR_HIP;
     hipFuncAttributes attr;
     if (rc == PMQA_OK && (hipFuncGetAttributes(&attr, schedule_kernel_symbol()) != hipSuccess ||
                           hipFuncGetAttributes(&attr, indexer_kernel_symbol()) != hipSuccess ||
@@ -113,11 +134,16 @@ int check_mqa_common(const void* q, const void* kv, int64_t page_stride, int32_t
   return PMQA_OK;
 }
 
+// Launches the kernels of one call on `stream`, one launch per pass over a
+// group of query slots (each pass writes its own output rows).  64 heads with
+// head_dim 128 take the kernels specialised for that shape, up to 4 slots a
+// pass; any other FP8 shape takes the general kernel, as many slots a pass as
+// its LDS budget for the query slice allows.
 int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride,
             int32_t num_pages, const float* w, const int32_t* seq_lens, const int32_t* bt,
-            int64_t bt_stride, int32_t batch, int32_t next_n, int variant, void* out,
-            int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
-            const int32_t* schedule, void* stream) {
+            int64_t bt_stride, int32_t batch, int32_t next_n, int32_t heads, int32_t head_dim,
+            int variant, void* out, int64_t out_row_stride, int32_t max_context,
+            int32_t out_dtype, const int32_t* schedule, void* stream) {
   DeviceInfo* d = nullptr;
   int rc = current_device_info(&d);
   if (rc != PMQA_OK) return rc;
@@ -136,12 +162,34 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   a.num_pages = num_pages;
   a.batch = batch;
   a.max_context = max_context;
-  a.pad_ = 0;
-  const size_t lds = mqa_ring_bytes(variant) + (size_t)(batch + 1) * sizeof(int);
-  const int grid = d->cus * blocks_per_cu(*d, next_n, variant, out_dtype, lds);
-  if (launch_mqa(a, next_n, variant, out_dtype, grid, lds, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
-    return PMQA_ERR_HIP;
+  a.next_n = next_n;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t prefix = (size_t)(batch + 1) * sizeof(int);
+  if (heads == 64 && head_dim == 128) {
+    const size_t lds = mqa_ring_bytes(variant) + prefix;
+    for (int s0 = 0; s0 < next_n; s0 += kFastSlots) {
+      a.slot0 = s0;
+      a.slots = next_n - s0 < kFastSlots ? next_n - s0 : kFastSlots;
+      const int grid = d->cus * blocks_per_cu(*d, a.slots, variant, out_dtype, lds);
+      if (launch_mqa(a, a.slots, variant, out_dtype, grid, lds, s) != hipSuccess)
+        return PMQA_ERR_HIP;
+    }
+    return PMQA_OK;
+  }
+  if (variant != PMQA_VARIANT_FP8) return PMQA_ERR_UNSUPPORTED;
+  const int ks = (head_dim + 127) / 128;
+  const int hp = (heads + 31) / 32 * 32;
+  int per = kAnyQueryBudget / (ks * 128 * hp);
+  if (per < 1) return PMQA_ERR_UNSUPPORTED;
+  for (int s0 = 0; s0 < next_n; s0 += per) {
+    a.slot0 = s0;
+    a.slots = next_n - s0 < per ? next_n - s0 : per;
+    const size_t lds = mqa_any_lds_bytes(ks, hp, a.slots) + prefix;
+    const int grid = d->cus * blocks_per_cu_any(*d, ks, out_dtype, lds);
+    if (launch_mqa_any(a, ks, out_dtype, grid, lds, s) != hipSuccess) return PMQA_ERR_HIP;
+  }
   return PMQA_OK;
 }
 
@@ -159,7 +207,8 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
                    int32_t max_context, int32_t out_dtype, int32_t acc_dtype,
                    const int32_t* schedule, void* stream) {
   if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
-  if (num_heads != 64 || head_dim != 128) return PMQA_ERR_UNSUPPORTED;
+  if (num_heads > kAnyMaxHeads || head_dim > kAnyMaxDim || head_dim % 16 != 0)
+    return PMQA_ERR_UNSUPPORTED;
   if (out_dtype != PMQA_F32 && out_dtype != PMQA_BF16) return PMQA_ERR_UNSUPPORTED;
   if (acc_dtype != PMQA_F32) return PMQA_ERR_UNSUPPORTED;
   int rc = check_mqa_common(q, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
@@ -167,8 +216,8 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
                             (int64_t)PMQA_PAGE_TOKENS * (head_dim + 4));
   if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
   return run_mqa(q, nullptr, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
-                 bt_stride, batch, next_n, PMQA_VARIANT_FP8, out, out_row_stride, max_context,
-                 out_dtype, schedule, stream);
+                 bt_stride, batch, next_n, num_heads, head_dim, PMQA_VARIANT_FP8, out,
+                 out_row_stride, max_context, out_dtype, schedule, stream);
 }
 
 int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
@@ -188,8 +237,8 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
   if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
   if (!q_sf) return PMQA_ERR_NULL;
   return run_mqa(q, q_sf, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
-                 bt_stride, batch, next_n, PMQA_VARIANT_MXFP4, out, out_row_stride, max_context,
-                 out_dtype, schedule, stream);
+                 bt_stride, batch, next_n, num_heads, head_dim, PMQA_VARIANT_MXFP4, out,
+                 out_row_stride, max_context, out_dtype, schedule, stream);
 }
 
 // Validation shared by both indexer entry points; key_bytes is the packed size
@@ -332,10 +381,11 @@ int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant) {
   if (rc != PMQA_OK) return rc;
   const DeviceInfo& d = g_dev[device];
   const int out = variant == PMQA_VARIANT_FP8 ? 0 : 1;  // the variant's default output
-  // one unit per resident workgroup: a workgroup pays the start-up of a range
-  // (page ids, first page loads, query) once per unit
+  // one unit per resident workgroup of the first pass of a 64-head, head_dim
+  // 128 call: a workgroup pays the start-up of a range (page ids, first page
+  // loads, query) once per unit
   const size_t lds = mqa_ring_bytes(variant) + sizeof(int);
-  return d.cus * blocks_per_cu(d, next_n, variant, out, lds);
+  return d.cus * blocks_per_cu(d, next_n < kFastSlots ? next_n : kFastSlots, variant, out, lds);
 }
 
 int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,

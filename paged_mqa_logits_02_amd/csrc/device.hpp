@@ -13,6 +13,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kPage = 64;   // tokens per KV page
 constexpr int kWave = 64;   // lanes per wavefront
@@ -56,6 +58,24 @@ __device__ __forceinline__ v16f mfma32_fp4(const v4i& a, int sa, const v4i& b, i
   v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, sa, 0,
                                                          sb);
+}
+
+// D[16x16] = A[16x32] * B[32x16] (+ C), f16 operands (8 per lane), fp32
+// accumulate; output layout as mfma_fp8.  Unlike the FP8 forms, whose sums keep
+// each product only down to 2^-13 of the largest product of the instruction
+// (measured on gfx950), this form sums at fp32 precision.
+__device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight e4m3 values (the bytes of lo, then of hi) widened to f16; exact for
+// every finite code, subnormals included (checked on all 256 codes).
+__device__ __forceinline__ v8h e4m3x8_to_f16(int lo, int hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // D[16x16] = A[16x32] * B[32x16] (+ C), bf16 operands (8 per lane), fp32 accumulate.

@@ -1,9 +1,11 @@
-// Paged MQA logits on gfx950.
+// Paged MQA logits on gfx950: the kernels for 64 heads and head_dim 128.
 //
 // Computes, per request b, query slot t and KV position p,
 //   logits[b*N+t, p] = s_p * sum_h w[b*N+t, h] * relu(q[b,t,h,:] . k_p)
 // (FlashInfer "flashinfer.attn_scores": introductory equation and the two
 // bullets after it; MXFP4 has no s_p and folds its block scales into q and k).
+// A launch scores `slots` (1..4) consecutive query slots, from slot0, of every
+// request's next_n; larger next_n runs as several launches.
 //
 // Work decomposition.  The work items of a call are (request, 64-token page)
 // pairs in request-major order.  A workgroup (4 wavefronts) is one "unit": it
@@ -22,12 +24,8 @@
 // registers: 16x16x128 f8f6f4 MFMA (heads x tokens), rectifier and weighted
 // head sum in registers, a cross-row reduction with permlane swaps, s_p, and
 // a coalesced store of exactly the page's 64 columns.
-#include "device.hpp"
-#include "pmqa_internal.h"
+#include "ring.hpp"
 
-#ifndef PMQA_STAGES
-#define PMQA_STAGES 4
-#endif
 #ifdef PMQA_WAVES_PER_EU
 #define PMQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PMQA_WAVES_PER_EU)))
 #else
@@ -35,61 +33,6 @@
 #endif
 
 namespace pmqa {
-
-constexpr int kStages = PMQA_STAGES;
-
-// --------------------------------------------------------------- schedule
-
-__device__ __forceinline__ int tiles_of(int L, int max_tiles) {
-  if (L <= 0) return 0;
-  int t = (L + kPage - 1) / kPage;
-  return t < max_tiles ? t : max_tiles;
-}
-
-// Exclusive prefix of per-request page counts into s_prefix[0..B]
-// (s_prefix[B] = total).  Whole workgroup; ends with a barrier.
-__device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int max_tiles,
-                             int* s_prefix, int* s_wsum) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave, nwave = nthr / kWave;
-  const int per = (B + nthr - 1) / nthr;
-  const int lo = tid * per;
-  const int hi = min(lo + per, B);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) {
-    int t = tiles_of(seq_lens[i], max_tiles);
-    s_prefix[i] = t;
-    sum += t;
-  }
-  int incl = wave_inclusive_scan(sum, lane);
-  if (lane == kWave - 1) s_wsum[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < nwave; ++w) {
-    int v = s_wsum[w];
-    base += (w < wave) ? v : 0;
-    total += v;
-  }
-  int run = base + incl - sum;
-  for (int i = lo; i < hi; ++i) {
-    int t = s_prefix[i];
-    s_prefix[i] = run;
-    run += t;
-  }
-  if (tid == 0) s_prefix[B] = total;
-  __syncthreads();
-}
-
-// Largest b in [0, B] with prefix[b] <= f.  For 0 <= f < prefix[B] the item f
-// lies in request b at page f - prefix[b].
-__device__ __forceinline__ int locate(const int* s_prefix, int B, long long f) {
-  int lo = 0, hi = B;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(s_prefix[mid]) <= f) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict__ seq_lens,
                                                        int B, int next_n, int variant,
@@ -120,92 +63,7 @@ __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict
   }
 }
 
-// ------------------------------------------------------- page staging (LDS)
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Lane i copies 16 (4) bytes from g to lds_base + 16i (4i); lds_base is uniform.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 4, 0, 0);
-}
-
-// Global loads the compiler does not track: it never inserts a wait for
-// them.  The query slice is loaded this way so that it can be issued ahead of
-// page loads and waited for with an exact count (wait_vmcnt / wait_page);
-// every use follows such a wait and settle().
-__device__ __forceinline__ v4i ldg_untracked(const void* p) {
-  v4i v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ int ldg_untracked_u8(const void* p) {
-  int v;
-  asm volatile("global_load_ubyte %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
-// Waits until at most N vector-memory loads of this wave are outstanding
-// (s_waitcnt vmcnt(N), other counters untouched).  The compiler's own waitcnt
-// tracking sees this wait; it does not track loads into LDS by itself.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the page ring: waits for this wave's LDS reads only.
-// Neither __syncthreads() nor a workgroup fence can be used here: both make
-// the compiler wait for every load into LDS still in flight, which would drain
-// the ring.  The empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Page layout per variant.  Key rows are stored in LDS with their 16-byte
-// chunks XOR-permuted by row (chunk c of row r sits in slot c ^ swz(r)).  The
-// permutations were chosen by measurement (rocprof SQ_LDS_BANK_CONFLICT = 0)
-// for both operand read patterns: 16 consecutive rows per 16 lanes (16x16
-// tiles) and 32 consecutive rows per 32 lanes (32x32 tiles).
-template <int VAR> struct PageLayout;
-
-template <> struct PageLayout<0> {       // FP8: 64 x 128 B keys, 64 fp32 scales
-  static constexpr int kRowBytes = 128;
-  static constexpr int kKeyBytes = kPage * kRowBytes;  // 8192
-  static constexpr int kStageBytes = kKeyBytes + kPage * 4;
-  static constexpr int kLoadsPerWave = 3;  // two 1 KB key chunks, one scale chunk
-  __device__ static int swz(int r) { return (r >> 1) & 7; }
-  // Wave w loads key rows 16w .. 16w+15 and scales of tokens 16w .. 16w+15.
-  // The per-lane byte offsets inside a page do not change from page to page;
-  // they are computed once, so a page's loads take a uniform base address and
-  // these offsets (no per-page vector arithmetic).
-  struct Lanes {
-    uint32_t key[2];
-    uint32_t scale;
-  };
-  __device__ static Lanes lanes(int wave, int lane) {
-    Lanes o;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * (2 * wave + i) + (lane >> 3);
-      o.key[i] = r * kRowBytes + 16 * ((lane & 7) ^ swz(r));
-    }
-    o.scale = kKeyBytes + 64 * wave + 4 * (lane & 15);
-    return o;
-  }
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
-                               int lane) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(page + o.key[i], stage + 8 * (2 * wave + i) * kRowBytes);
-    if (lane < 16) dma4(page + o.scale, stage + kKeyBytes + 64 * wave);
-  }
-};
+// ---------------------------------------------------- MXFP4 page and operands
 
 template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4 e8m0
   static constexpr int kRowBytes = 64;
@@ -231,30 +89,6 @@ template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4
   }
 };
 
-// ------------------------------------------------------------ operands
-
-// MFMA operand fragment of one 16-row tile.  The K dimension (head_dim) is
-// split over lanes identically for the query (A) and key (B) operand, so every
-// product pairs matching d.
-template <int VAR> struct Frag;
-
-// FP8: lane l holds d in [16g, 16g+16) and [64+16g, 64+16g+16), g = l>>4.
-template <> struct Frag<0> {
-  v8i v;
-  __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
-    v4i lo = ldg_untracked(row + 16 * g);
-    v4i hi = ldg_untracked(row + 64 + 16 * g);
-    v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
-    const int sw = PageLayout<0>::swz(r);
-    const uint8_t* row = stage + r * PageLayout<0>::kRowBytes;
-    v4i lo = *reinterpret_cast<const v4i*>(row + 16 * (g ^ sw));
-    v4i hi = *reinterpret_cast<const v4i*>(row + 16 * ((4 + g) ^ sw));
-    v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-};
-
 // MXFP4: lane l holds the 32-element block g = l>>4 (16 packed bytes) and that
 // block's e8m0 code.
 template <> struct Frag<1> {
@@ -270,9 +104,6 @@ template <> struct Frag<1> {
   }
 };
 
-__device__ __forceinline__ v4f mma(const Frag<0>& q, const Frag<0>& k) {
-  return mfma_fp8(q.v, k.v, (v4f){0.f, 0.f, 0.f, 0.f});
-}
 __device__ __forceinline__ v4f mma(const Frag<1>& q, const Frag<1>& k) {
   return mfma_fp4(q.v, q.sf, k.v, k.sf, (v4f){0.f, 0.f, 0.f, 0.f});
 }
@@ -342,14 +173,6 @@ template <int TW, int VAR> struct QueryFrag {
   v4f w[4][TW];        // w[mt][t][i] = weight of head 16mt + 4(l>>4) + i
 };
 
-// Marks x as redefined here: the empty asm reads and rewrites it, so no use
-// of x can be scheduled above this point.  Placed after the explicit wait for
-// the (untracked) loads of x, it makes every use see the loaded value.
-template <typename T>
-__device__ __forceinline__ void settle(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
 template <int TW, int VAR>
 __device__ __forceinline__ void settle_query(QueryFrag<TW, VAR>& qf) {
 #pragma unroll
@@ -371,11 +194,11 @@ __device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs
   for (int t = 0; t < TW; ++t) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const long long head_row = ((long long)(b * N + t0 + t) * 64 + 16 * mt + r);
+      const long long head_row = (row_of(a, b, t0 + t) * 64 + 16 * mt + r);
       qf.q[mt][t].load_global(a.q + head_row * kQRow, g);
       if constexpr (VAR == 1) qf.q[mt][t].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
       qf.w[mt][t] = __builtin_bit_cast(
-          v4f, ldg_untracked(a.w + (long long)(b * N + t0 + t) * 64 + 16 * mt + 4 * g));
+          v4f, ldg_untracked(a.w + row_of(a, b, t0 + t) * 64 + 16 * mt + 4 * g));
     }
   }
 }
@@ -407,7 +230,7 @@ __device__ __forceinline__ void load_query(WideQuery<VAR>& qf, const MqaArgs& a,
                                            int lane) {
   const int h = lane >> 5, r = lane & 31;
   constexpr int kQRow = VAR == 0 ? 128 : 64;
-  const long long slot = (long long)b * N + t0;
+  const long long slot = row_of(a, b, t0);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const long long head_row = slot * 64 + 32 * mt + r;
@@ -423,20 +246,6 @@ __device__ __forceinline__ void load_query(WideQuery<VAR>& qf, const MqaArgs& a,
 }
 
 // ------------------------------------------------------------- main kernel
-
-// Stores one logit; an output that depends on an out-of-range page id is a
-// quiet NaN, written as a bit pattern (this file is compiled without NaN
-// semantics for arithmetic, so no NaN is ever produced by arithmetic).
-template <int OUTT>
-__device__ __forceinline__ void store_logit(void* out, long long idx, float v, bool valid) {
-  if constexpr (OUTT == 0) {
-    const uint32_t bits = valid ? __float_as_uint(v) : 0x7FC00000u;
-    reinterpret_cast<uint32_t*>(out)[idx] = bits;
-  } else {
-    const uint16_t bits = valid ? f32_to_bf16_rne(v) : (uint16_t)0x7FC0u;
-    reinterpret_cast<uint16_t*>(out)[idx] = bits;
-  }
-}
 
 template <int VAR>
 __device__ __forceinline__ float stage_scale(const uint8_t* stage, int token) {
@@ -491,7 +300,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR
     for (int t = 0; t < TW; ++t) {
       float v = row_transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
       v *= stage_scale<VAR>(stage, lane);
-      store_logit<OUTT>(a.out, (long long)(b * N + t0 + t) * a.out_row_stride + col0 + lane, v,
+      store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + lane, v,
                         valid);
     }
   } else if constexpr (SW == 2) {
@@ -507,7 +316,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR
       const int token = 16 * (s0 + (lane >> 5)) + rr;
       v *= stage_scale<VAR>(stage, token);
       if ((g & 1) == 0)
-        store_logit<OUTT>(a.out, (long long)(b * N + t0 + t) * a.out_row_stride + col0 + token, v,
+        store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + token, v,
                           valid);
     }
   } else if constexpr (TW == 1) {
@@ -515,7 +324,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR
     const int token = 16 * s0 + rr;
     v *= stage_scale<VAR>(stage, token);
     if (g == 0)
-      store_logit<OUTT>(a.out, (long long)(b * N + t0) * a.out_row_stride + col0 + token, v, valid);
+      store_logit<OUTT>(a.out, row_of(a, b, t0) * a.out_row_stride + col0 + token, v, valid);
   } else {
     static_assert((TW == 3 || TW == 4) && SW == 1, "unsupported split");
     // row g ends with slot g
@@ -524,7 +333,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<WaveSplit<N>::TW, VAR
     const int token = 16 * s0 + rr;
     v *= stage_scale<VAR>(stage, token);
     if (g < TW)
-      store_logit<OUTT>(a.out, (long long)(b * N + g) * a.out_row_stride + col0 + token, v, valid);
+      store_logit<OUTT>(a.out, row_of(a, b, g) * a.out_row_stride + col0 + token, v, valid);
   }
 }
 
@@ -571,35 +380,8 @@ __device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8
   float x = part[0], y = part[NT - 1];
   swap32(x, y);
   const float v = (x + y) * sp;  // NT == 2: lane l has token l; else lanes < 32 have it
-  const long long idx = (long long)(b * N + t0) * a.out_row_stride + (long long)j * kPage + token;
+  const long long idx = row_of(a, b, t0) * a.out_row_stride + (long long)j * kPage + token;
   if (NT == 2 || h == 0) store_logit<OUTT>(a.out, idx, v, valid);
-}
-
-// Values read from LDS are wave-uniform here; saying so keeps the cursors in
-// scalar registers and the page-id fetch a scalar load.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ int tiles_at(const int* s_prefix, int b) {
-  return uniform(s_prefix[b + 1] - s_prefix[b]);
-}
-
-__device__ __forceinline__ bool page_ok(const MqaArgs& a, int pg) {
-  return (unsigned)pg < (unsigned)a.num_pages;
-}
-
-// Waits for the loads of the page scored now, given how many pages were
-// issued after it (`ahead`, 0 .. kMax).  The steady state (kMax pages ahead)
-// is tested first; fewer pages are ahead only at the end of a range.
-template <int LPI, int kMax>
-__device__ __forceinline__ void wait_page(int ahead) {
-  static_assert(kMax * LPI < 64, "vmcnt range");
-  if (ahead >= kMax) {
-    wait_vmcnt<kMax * LPI>();
-  } else if constexpr (kMax > 1) {
-    wait_page<LPI, kMax - 1>(ahead);
-  } else {
-    wait_vmcnt<0>();
-  }
 }
 
 template <bool Wide, int N, int VAR> struct QueryPick { using type = QueryFrag<WaveSplit<N>::TW, VAR>; };
@@ -610,33 +392,6 @@ template <int N, int VAR, typename Q>
 __device__ __forceinline__ void load_query_any(Q& qf, const MqaArgs& a, int b, int t0, int lane) {
   if constexpr (WaveSplit<N>::kWide) load_query<N, VAR>(qf, a, b, t0, lane);
   else load_query<N, WaveSplit<N>::TW, VAR>(qf, a, b, t0, lane);
-}
-
-#ifndef PMQA_PID_TABLE
-#define PMQA_PID_TABLE 512
-#endif
-constexpr int kPidTable = PMQA_PID_TABLE;  // page ids of the next items, in LDS
-
-// Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+kPidTable-1 (up
-// to f_end); entries past the end are not written.  (b, j) is item f's
-// request and page.  Thread t walks from there to item f+t, request by
-// request (a unit spans few requests, so this is a few LDS reads).  Whole
-// workgroup; the caller places the barrier.
-__device__ __forceinline__ void fill_pid_table(const MqaArgs& a, const int* s_prefix, int* s_pid,
-                                               long long f, long long f_end, int b, int j) {
-  for (int t = threadIdx.x; t < kPidTable; t += blockDim.x) {
-    if (f + t < f_end) {
-      int bb = b, jj = j + t, pid = -1;
-      while (bb < a.batch) {
-        const int tiles = s_prefix[bb + 1] - s_prefix[bb];
-        if (jj < tiles) break;
-        jj -= tiles;
-        ++bb;
-      }
-      if (bb < a.batch) pid = a.bt[(long long)bb * a.bt_stride + jj];
-      s_pid[t] = pid;
-    }
-  }
 }
 
 // Scores flat items f0 .. f0+count-1, the whole workgroup together.
@@ -776,7 +531,7 @@ __global__ void __launch_bounds__(256) PMQA_OCCUPANCY
   const int unit = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   const int32_t* sc = a.schedule;
-  const bool use_sched = sc != nullptr && sc[0] == kSchedMagic && sc[2] == N &&
+  const bool use_sched = sc != nullptr && sc[0] == kSchedMagic && sc[2] == a.next_n &&
                          sc[3] == VAR && sc[4] == a.max_context && sc[5] == a.batch &&
                          sc[1] > 0;
   if (use_sched) {
@@ -805,9 +560,9 @@ static const void* kernel_ptr() {
   return reinterpret_cast<const void*>(&mqa_logits_kernel<N, VAR, OUTT>);
 }
 
-const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype) {
+const void* mqa_kernel_symbol(int slots, int variant, int out_dtype) {
 #define PMQA_K(n)                                                                         \
-  if (next_n == n) {                                                                      \
+  if (slots == n) {                                                                       \
     if (variant == 0) return out_dtype == 0 ? kernel_ptr<n, 0, 0>() : kernel_ptr<n, 0, 1>(); \
     return out_dtype == 0 ? kernel_ptr<n, 1, 0>() : kernel_ptr<n, 1, 1>();               \
   }
@@ -823,9 +578,9 @@ size_t mqa_ring_bytes(int variant) {
   return variant == 0 ? (size_t)ring_bytes<1, 0>() : (size_t)ring_bytes<1, 1>();
 }
 
-hipError_t launch_mqa(const MqaArgs& a, int next_n, int variant, int out_dtype, int grid,
+hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, int grid,
                       size_t lds_bytes, hipStream_t stream) {
-  const void* fn = mqa_kernel_symbol(next_n, variant, out_dtype);
+  const void* fn = mqa_kernel_symbol(slots, variant, out_dtype);
   if (!fn) return hipErrorInvalidValue;
   const uint8_t* q = a.q;
   const uint8_t* q_sf = a.q_sf;

@@ -13,11 +13,11 @@ constexpr int kMaxBatch = 8192;           // prefix of page counts kept in LDS
 
 // Arguments of the MQA logits kernels (FP8 and MXFP4).
 struct MqaArgs {
-  const uint8_t* q;        // fp8 [B,N,64,128] or packed fp4 [B,N,64,64]
+  const uint8_t* q;        // fp8 [B,N,H,D] or packed fp4 [B,N,64,64]
   const uint8_t* q_sf;     // e8m0 [B,N,64,4] (MXFP4 only)
   const uint8_t* kv;       // pages
   long long page_stride;   // bytes between pages
-  const float* w;          // [B*N, 64]
+  const float* w;          // [B*N, H]
   const int32_t* seq_lens; // [B]
   const int32_t* bt;       // [B, bt_stride]
   long long bt_stride;
@@ -27,7 +27,11 @@ struct MqaArgs {
   int num_pages;
   int batch;
   int max_context;
-  int pad_;
+  int next_n;              // N: query slots per request (row b*N + t of q, w and out)
+  int slot0;               // first slot scored by this launch (a pass over slots)
+  int slots;               // slots scored by this launch
+  int heads;               // H
+  int head_dim;            // D (bytes of an FP8 key row)
 };
 
 struct IdxArgs {
@@ -52,13 +56,26 @@ struct IdxArgs {
   int max_context;
 };
 
-const void* mqa_kernel_symbol(int next_n, int variant, int out_dtype);
+// Kernels for 64 heads and head_dim 128, one instance per slot count of a
+// pass (1..kFastSlots).
+constexpr int kFastSlots = 4;
+const void* mqa_kernel_symbol(int slots, int variant, int out_dtype);
 size_t mqa_ring_bytes(int variant);  // LDS of the page ring (before the request prefix)
+
+// FP8 kernels for any head count and head_dim: ks = head_dim planes of 128 B
+// (1 or 2).  LDS: ring, query slice, weights, then the request prefix.
+constexpr int kAnyMaxHeads = 128;
+constexpr int kAnyMaxDim = 256;
+constexpr int kAnyQueryBudget = 32768;  // bytes of query slice in LDS per pass
+const void* mqa_any_kernel_symbol(int ks, int out_dtype);
+size_t mqa_any_lds_bytes(int ks, int heads_padded, int slots);  // excluding the prefix
+hipError_t launch_mqa_any(const MqaArgs& a, int ks, int out_dtype, int grid, size_t lds_bytes,
+                          hipStream_t stream);
 const void* schedule_kernel_symbol();
 const void* indexer_kernel_symbol();
 const void* indexer_nvfp4_kernel_symbol();
 
-hipError_t launch_mqa(const MqaArgs& a, int next_n, int variant, int out_dtype, int grid,
+hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, int grid,
                       size_t lds_bytes, hipStream_t stream);
 hipError_t launch_schedule(const int32_t* seq_lens, int B, int next_n, int variant,
                            int max_context, int U, int32_t* sched, hipStream_t stream);

@@ -1,7 +1,9 @@
 """The C-ABI library: it loads, exports every function include/pmqa.h declares,
 and its host-side validation returns the documented status codes.  None of
 these calls reaches the GPU (each is rejected, or is a no-op, before any
-launch), so they run without one."""
+launch), so they run without one.  Every case here must stay a rejection or a
+no-op: the addresses are fake, so an accepted call would launch kernels on
+them."""
 import ctypes
 import os
 import re
@@ -75,8 +77,10 @@ def _fp8(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,rc", [
-    (dict(H=32), UNSUP), (dict(D=64), UNSUP), (dict(H=0), SHAPE), (dict(acc=1), UNSUP),
-    (dict(od=2), UNSUP), (dict(N=5), UNSUP), (dict(N=0), SHAPE), (dict(maxc=100), SHAPE),
+    (dict(H=129), UNSUP), (dict(D=72), UNSUP), (dict(D=272, ps=64 * 276), UNSUP),
+    (dict(H=0), SHAPE), (dict(D=0), SHAPE), (dict(acc=1), UNSUP),
+    (dict(od=2), UNSUP), (dict(N=9), UNSUP), (dict(N=65), SHAPE), (dict(N=0), SHAPE),
+    (dict(maxc=100), SHAPE), (dict(H=32, D=256), SHAPE), (dict(D=64, ps=64 * 68 - 16), SHAPE),
     (dict(maxc=-64), SHAPE), (dict(B=-1), SHAPE), (dict(B=8193), SHAPE),
     (dict(q=None), NULL), (dict(kv=None), NULL), (dict(out=None), NULL), (dict(sl=None), NULL),
     (dict(ps=8440), SHAPE), (dict(ps=8448 + 8), ALIGN), (dict(btw=3), SHAPE),
@@ -102,7 +106,7 @@ def _mx(lib, **kw):
 @pytest.mark.parametrize("kw,rc", [
     (dict(sfv=16), UNSUP), (dict(inter=1), UNSUP), (dict(H=32), UNSUP), (dict(D=256), UNSUP),
     (dict(qsf=None), NULL), (dict(ps=4340), SHAPE), (dict(ps=4352 + 4), ALIGN),
-    (dict(N=5), UNSUP), (dict(B=0), OK),
+    (dict(N=9), UNSUP), (dict(B=0), OK),
 ])
 def test_mxfp4_validation(pm, kw, rc):
     assert _mx(pm.library(), **kw) == rc
@@ -153,7 +157,7 @@ def test_indexer_nvfp4_validation(pm, kw, rc):
 
 def test_schedule_validation(pm):
     lib = pm.library()
-    assert lib.mqa_logits_schedule(FAKE, 4, 5, 0, 256, 8, FAKE, None) == UNSUP
+    assert lib.mqa_logits_schedule(FAKE, 4, 9, 0, 256, 8, FAKE, None) == UNSUP
     assert lib.mqa_logits_schedule(FAKE, 4, 1, 2, 256, 8, FAKE, None) == UNSUP
     assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 100, 8, FAKE, None) == SHAPE
     assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 256, -1, FAKE, None) == SHAPE

@@ -18,9 +18,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def drains_before_mfma(asm):
+def drains_before_mfma(asm, kernel="17mqa_logits_kernel"):
     bad = []
-    kernels = re.findall(r"^(_ZN4pmqa17mqa_logits_kernel\S+):[^\n]*\n(.*?)^\s+s_endpgm", asm,
+    kernels = re.findall(r"^(_ZN4pmqa" + kernel + r"\S+):[^\n]*\n(.*?)^\s+s_endpgm", asm,
                          re.S | re.M)
     assert kernels, "no logits kernels found in the assembly"
     for name, body in kernels:
@@ -31,7 +31,15 @@ def drains_before_mfma(asm):
     return kernels, bad
 
 
-def test_page_loop_has_no_full_drain_before_the_matrix_work():
+# source, mangled kernel name stem, instances: the 64-head kernels (slots 1..4
+# x {fp8, mxfp4} x {fp32, bf16 out}) and the general FP8 kernels (1 or 2
+# planes x {fp32, bf16 out})
+SOURCES = [("mqa_logits.hip", "17mqa_logits_kernel", 16),
+           ("mqa_any.hip", "21mqa_logits_any_kernel", 4)]
+
+
+@pytest.mark.parametrize("src,kernel,count", SOURCES, ids=[s[0] for s in SOURCES])
+def test_page_loop_has_no_full_drain_before_the_matrix_work(src, kernel, count):
     import sys
     sys.path.insert(0, ROOT)
     from paged_mqa_logits_02_amd import build
@@ -39,16 +47,16 @@ def test_page_loop_has_no_full_drain_before_the_matrix_work():
         cc = build.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    src = os.path.join(build.CSRC, "mqa_logits.hip")
+    path = os.path.join(build.CSRC, src)
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
-        flags = [f for f in build.compile_flags("mqa_logits.hip") if f != "-fPIC"]
-        r = subprocess.run([cc] + flags + ["--cuda-device-only", "-S", src, "-o", out],
+        flags = [f for f in build.compile_flags(src) if f != "-fPIC"]
+        r = subprocess.run([cc] + flags + ["--cuda-device-only", "-S", path, "-o", out],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         asm = open(out).read()
-    kernels, bad = drains_before_mfma(asm)
-    assert len(kernels) == 16  # next_n 1..4 x {fp8, mxfp4} x {fp32, bf16 out}
+    kernels, bad = drains_before_mfma(asm, kernel)
+    assert len(kernels) == count
     assert not bad, "vmcnt(0) before the matrix work in: %s" % sorted(set(bad))
 
 
