@@ -1,4 +1,4 @@
-"""Benchmark: FP8 paged MQA logits (H=64, d=128) on one MI355X.
+"""Benchmark: FP8 paged MQA logits (H=64, d=128; other workloads by name) on one MI355X.
 
 One step = one whole call of the hot path on the synthetic workload: the
 work split (computed on the GPU, either inside the logits kernel or by the
@@ -16,7 +16,7 @@ latency when launches are short); --graph captures the K steps into a HIP
 graph and times one replay.
 
 Prints one JSON line (rank 0, one GPU).  Usage:
-  python bench.py [--steps K] [--warmup W] [--workload verify_fp8|decode_fp8|mxfp4]
+  python bench.py [--steps K] [--warmup W] [--workload verify_fp8|decode_fp8|mxfp4|...]
                   [--mode in_call|schedule] [--graph|--launch-events] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain copy of known size (counter scale)
 """
@@ -31,8 +31,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "KV positions/sec and achieved HBM GB/s, fp8 paged MQA logits H=64 d=128"
-METRIC_MXFP4 = "KV positions/sec and achieved HBM GB/s, mxfp4 paged MQA logits H=64 d=128"
+METRIC_FMT = "KV positions/sec and achieved HBM GB/s, %s paged MQA logits H=%d d=%d"
+METRIC = METRIC_FMT % ("fp8", 64, 128)
+METRIC_MXFP4 = METRIC_FMT % ("mxfp4", 64, 128)
 METRIC_INDEXER = "KV positions/sec and achieved HBM GB/s, one-head bf16 indexer scores d=128"
 METRIC_INDEXER_NVFP4 = ("KV positions/sec and achieved HBM GB/s, one-head nvfp4 indexer scores "
                         "d=128")
@@ -43,6 +44,9 @@ WORKLOADS = {
     "verify_fp8": "B=128, next_n=4, H=64, d=128, page 64, seq_lens uniform 4K..64K, fp32 out",
     "decode_fp8": "B=64, next_n=1, H=64, d=128, page 64, seq_lens log-uniform 1K..32K, fp32 out",
     "mxfp4": "B=64, next_n=2, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
+    "verify_fp8_n8": "B=64, next_n=8, H=64, d=128, page 64, seq_lens uniform 4K..64K, fp32 out",
+    "verify_fp8_h32": "B=128, next_n=2, H=32, d=128, page 64, seq_lens uniform 4K..64K, "
+                      "fp32 out",
     "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
     "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "
@@ -50,16 +54,36 @@ WORKLOADS = {
 }
 
 
-def algorithmic_bytes_per_position(variant, next_n, out_bytes):
+def algorithmic_bytes_per_position(variant, next_n, out_bytes, head_dim=128):
     """Bytes the method must move per KV position (page-tail padding, query,
     weight and block-table reads excluded): the key, its scale, one output
     per query slot."""
     if variant == "fp8":
-        return 128 + 4 + next_n * out_bytes
-    return 64 + 4 + next_n * out_bytes
+        return head_dim + 4 + next_n * out_bytes
+    return head_dim // 2 + head_dim // 32 + next_n * out_bytes
+
+
+def launch_slots(variant, next_n, num_heads, head_dim):
+    """Query slots of each kernel launch of one call, as the library splits
+    them: up to 4 per launch with 64 heads x 128; otherwise (FP8) as many as
+    a 32 KB query slice of the heads padded to 32 holds."""
+    if num_heads == 64 and head_dim == 128:
+        per = 4
+    else:
+        per = 32768 // (-(-head_dim // 128) * 128 * (-(-num_heads // 32) * 32))
+    return [min(per, next_n - s) for s in range(0, next_n, per)]
+
+
+def launch_bytes_per_position(variant, next_n, out_bytes, num_heads, head_dim):
+    """Algorithmic bytes per KV position summed over the launches of a call:
+    every launch reads the key and its scale and writes its own slots."""
+    return sum(algorithmic_bytes_per_position(variant, n, out_bytes, head_dim)
+               for n in launch_slots(variant, next_n, num_heads, head_dim))
 
 
 KERNEL_SOURCES = ["paged_mqa_logits_02_amd/csrc/mqa_logits.hip",
+                  "paged_mqa_logits_02_amd/csrc/mqa_any.hip",
+                  "paged_mqa_logits_02_amd/csrc/ring.hpp",
                   "paged_mqa_logits_02_amd/csrc/device.hpp",
                   "paged_mqa_logits_02_amd/csrc/pmqa_internal.h",
                   "paged_mqa_logits_02_amd/build.py"]
@@ -382,13 +406,19 @@ def main():
 
     traffic = counter_traffic(args.workload)
     positions = inp.kv_positions()
-    bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes)
+    bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes, inp.head_dim)
+    slots = launch_slots(inp.variant, inp.next_n, inp.num_heads, inp.head_dim)
+    lbpp = launch_bytes_per_position(inp.variant, inp.next_n, out_bytes, inp.num_heads,
+                                     inp.head_dim)
     alg_bytes = positions * bpp
-    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
+    # roofline of the logits kernel: algorithmic bytes of every launch of a
+    # call (each launch reads the keys) over the call's duration, i.e. the
+    # average over its launches (equal-size launches)
+    achieved = positions * lbpp / (kern_avg * 1e-3) / 1e9
     value = positions * K / (total_ms * 1e-3)
 
     line = {
-        "metric": METRIC if variant == 0 else METRIC_MXFP4,
+        "metric": METRIC_FMT % (inp.variant, inp.num_heads, inp.head_dim),
         "value": value,
         "unit": "KV positions/s",
         "n_gpus": 1,
@@ -408,19 +438,24 @@ def main():
             "head_dim": inp.head_dim, "max_context": inp.max_context,
             "kv_positions": positions, "pages": int(inp.num_pages),
             "schedule": args.mode, "kv_replicas": R, "units": U,
+            "products": ("fp8 MFMA" if (inp.num_heads, inp.head_dim) == (64, 128) else
+                         "f16 MFMA of exactly widened e4m3"),
             "timing": ("graph of the %d steps, events around one replay" % K if args.graph else
                        "host launches of prepared calls, " +
                        ("events around every launch" if args.launch_events else
                         "events around the %d launches" % K)),
             "kernel_ms_avg": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
             "algorithmic_bytes_per_position": bpp,
-            "algorithmic_bytes_per_launch": alg_bytes,
+            "launch_slots": slots,
+            "launch_bytes_per_position": lbpp,
+            "algorithmic_bytes_per_launch": positions * lbpp / len(slots),
             "counter_bytes_per_launch": traffic,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None if traffic is None else traffic / (kern_avg * 1e-3) / 1e9,
+            "traffic": (None if traffic is None else
+                        traffic * len(slots) / (kern_avg * 1e-3) / 1e9),
         },
     }
     if not args.no_cpu_baseline:
