@@ -73,8 +73,8 @@ template <int KS> struct PlaneLayout {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        dma16(page + o.key[ks][i], stage + ks * kPlaneBytes + 8 * (2 * wave + i) * 128);
-    if (lane < 16) dma4(page + o.scale, stage + kKeyBytes + 64 * wave);
+        dma16_page(page + o.key[ks][i], stage + ks * kPlaneBytes + 8 * (2 * wave + i) * 128);
+    if (lane < 16) dma4_page(page + o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 

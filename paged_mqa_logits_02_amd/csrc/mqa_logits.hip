@@ -84,8 +84,8 @@ template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4
   }
   __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
                                int lane) {
-    dma16(page + o.key, stage + 16 * wave * kRowBytes);
-    if (lane < 16) dma4(page + o.scale, stage + kKeyBytes + 64 * wave);
+    dma16_page(page + o.key, stage + 16 * wave * kRowBytes);
+    if (lane < 16) dma4_page(page + o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 
