@@ -197,9 +197,11 @@ int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t ro
  * computed on the device, which a caller may build once and pass back.)
  *
  * Splits the (request, 64-token page) work items of one call, in request-major
- * order, into num_units contiguous ranges of near-equal length and writes the
- * opaque int32 buffer `schedule` of mqa_logits_schedule_ints(num_units)
- * entries.  num_units in 1 .. 1<<20; 0 means mqa_logits_num_units(current
+ * order, into num_units contiguous ranges and writes the opaque int32 buffer
+ * `schedule` of mqa_logits_schedule_ints(num_units) entries.  The ranges are
+ * of near-equal length, except that with next_n >= 4 FP8 and the default unit
+ * count the units of workgroups dispatched earlier on a compute unit get
+ * proportionally more items (the same split the kernel makes by itself).  num_units in 1 .. 1<<20; 0 means mqa_logits_num_units(current
  * device, next_n, variant).  The result depends only on seq_lens, batch,
  * next_n, variant and max_context; it must be rebuilt whenever seq_lens
  * changes (including on every graph replay).

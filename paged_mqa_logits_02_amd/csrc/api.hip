@@ -165,6 +165,8 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   a.next_n = next_n;
   a.heads = heads;
   a.head_dim = head_dim;
+  a.cus = d->cus;
+  a.split_skew = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t prefix = (size_t)(batch + 1) * sizeof(int);
   if (heads == 64 && head_dim == 128) {
@@ -172,6 +174,7 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
     for (int s0 = 0; s0 < next_n; s0 += kFastSlots) {
       a.slot0 = s0;
       a.slots = next_n - s0 < kFastSlots ? next_n - s0 : kFastSlots;
+      a.split_skew = split_skew_for(a.slots, variant);
       const int grid = d->cus * blocks_per_cu(*d, a.slots, variant, out_dtype, lds);
       if (launch_mqa(a, a.slots, variant, out_dtype, grid, lds, s) != hipSuccess)
         return PMQA_ERR_HIP;
@@ -400,18 +403,20 @@ int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, 
   if (!schedule || (batch > 0 && !seq_lens)) return PMQA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(schedule) | reinterpret_cast<uintptr_t>(seq_lens)) & 3)
     return PMQA_ERR_ALIGN;
+  DeviceInfo* d = nullptr;
+  int rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
   if (num_units == 0) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PMQA_ERR_HIP;
     num_units = mqa_logits_num_units(dev, next_n, variant);
     if (num_units < 0) return num_units;
-  } else {
-    DeviceInfo* d = nullptr;
-    int rc = current_device_info(&d);
-    if (rc != PMQA_OK) return rc;
   }
-  if (launch_schedule(seq_lens, batch, next_n, variant, max_context, num_units, schedule,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
+  // the split of the call's first launch (64 heads x 128): the units are the
+  // workgroups of that launch when num_units is the default
+  const int skew = split_skew_for(next_n < kFastSlots ? next_n : kFastSlots, variant);
+  if (launch_schedule(seq_lens, batch, next_n, variant, max_context, num_units, d->cus, skew,
+                      schedule, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PMQA_ERR_HIP;
   return PMQA_OK;
 }

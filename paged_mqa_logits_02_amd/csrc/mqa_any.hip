@@ -303,8 +303,8 @@ __global__ void __launch_bounds__(256)
     }
   } else {
     const long long P = uniform(s_prefix[a.batch]);
-    const long long f0 = (long long)unit * P / G;
-    const long long f1 = (long long)(unit + 1) * P / G;
+    const long long f0 = split_point(unit, G, a.cus, a.split_skew, P);
+    const long long f1 = split_point(unit + 1, G, a.cus, a.split_skew, P);
     if (f1 > f0)
       process_range_any<KS, OUTT>(a, s_prefix, s_pid, ring, q_lds, w_lds, f0, (int)(f1 - f0));
   }

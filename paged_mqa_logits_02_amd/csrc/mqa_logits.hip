@@ -36,8 +36,8 @@ namespace pmqa {
 
 __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict__ seq_lens,
                                                        int B, int next_n, int variant,
-                                                       int max_context, int U,
-                                                       int32_t* __restrict__ sched) {
+                                                       int max_context, int U, int cus,
+                                                       int skew, int32_t* __restrict__ sched) {
   extern __shared__ int s_prefix[];
   __shared__ int s_wsum[16];
   build_prefix(seq_lens, B, max_context / kPage, s_prefix, s_wsum);
@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict
     sched[7] = 0;
   }
   for (int u = threadIdx.x; u <= U; u += blockDim.x) {
-    long long f = (long long)u * P / U;
+    long long f = split_point(u, U, cus, skew, P);
     int b = (u == U) ? B : locate(s_prefix, B, f);
     int j = (u == U) ? 0 : (int)(f - s_prefix[b]);
     int32_t* e = sched + kSchedHeader + 3 * u;
@@ -547,8 +547,8 @@ __global__ void __launch_bounds__(256) PMQA_OCCUPANCY
     }
   } else {
     const long long P = uniform(s_prefix[a.batch]);
-    const long long f0 = (long long)unit * P / G;
-    const long long f1 = (long long)(unit + 1) * P / G;
+    const long long f0 = split_point(unit, G, a.cus, a.split_skew, P);
+    const long long f1 = split_point(unit + 1, G, a.cus, a.split_skew, P);
     if (f1 > f0) process_range<N, VAR, OUTT>(a, s_prefix, s_pid, ring, f0, (int)(f1 - f0));
   }
 }
@@ -595,10 +595,11 @@ hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, i
 }
 
 hipError_t launch_schedule(const int32_t* seq_lens, int B, int next_n, int variant,
-                           int max_context, int U, int32_t* sched, hipStream_t stream) {
+                           int max_context, int U, int cus, int skew, int32_t* sched,
+                           hipStream_t stream) {
   const size_t lds = (size_t)(B + 1) * sizeof(int);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kBlockThreads), lds, stream, seq_lens, B,
-                     next_n, variant, max_context, U, sched);
+                     next_n, variant, max_context, U, cus, skew, sched);
   return hipGetLastError();
 }
 

@@ -67,6 +67,30 @@ __device__ __forceinline__ int locate(const int* s_prefix, int B, long long f) {
   return lo;
 }
 
+// In-call work split.  Unit u (the workgroups renumbered XCD-major: the
+// dispatcher deals blocks to the 8 XCDs round-robin, unit = (block % 8) *
+// (G / 8) + block / 8) takes items [split_point(u), split_point(u + 1)).
+// When the grid is R workgroups per CU (G = R * cus), the blocks are
+// dispatched in R rounds of one per CU (round = block / cus, which is
+// (u % (G/8)) / (cus/8) in unit terms), and the hardware's issue priority for
+// older waves makes a CU's round-0 workgroup run fastest and its last-round
+// workgroup slowest.  Weight w_r = 1024 + skew * (R-1-2r) / (R-1) per unit of
+// round r (skew in 1024ths) gives the early rounds more items so that a CU's
+// workgroups finish together; skew 0 (or any other grid) is the equal split.
+__device__ __forceinline__ long long split_weight_before(int u, int G, int cus, int skew) {
+  const int R = G / cus, per = cus / 8, chunk = G / 8;
+  long long wchunk = 0;
+  for (int r = 0; r < R; ++r) wchunk += (long long)per * (1024 + skew * (R - 1 - 2 * r) / (R - 1));
+  const int y = u % chunk, ry = y / per;
+  long long c = (long long)(u / chunk) * wchunk;
+  for (int r = 0; r < ry; ++r) c += (long long)per * (1024 + skew * (R - 1 - 2 * r) / (R - 1));
+  return c + (long long)(y % per) * (1024 + skew * (R - 1 - 2 * ry) / (R - 1));
+}
+__device__ __forceinline__ long long split_point(int u, int G, int cus, int skew, long long P) {
+  if (skew <= 0 || skew >= 1024 || cus < 8 || cus % 8 != 0 || G % cus != 0 || G / cus < 2) return (long long)u * P / G;
+  return split_weight_before(u, G, cus, skew) * P / split_weight_before(G, G, cus, skew);
+}
+
 // ------------------------------------------------------- page staging (LDS)
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
