@@ -262,8 +262,12 @@ def _mid_inputs(variant="fp8", next_n=2, seed=300):
 
 
 @pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
-def test_schedule_any_unit_count_bit_identical(variant):
-    inp = _mid_inputs(variant)
+@pytest.mark.parametrize("next_n", [2, 4])
+def test_schedule_any_unit_count_bit_identical(variant, next_n):
+    """Any unit count, and the default one (next_n 4 FP8: the split weighted
+    by dispatch round, in the kernel and in the schedule), gives the in-call
+    result bit for bit."""
+    inp = _mid_inputs(variant, next_n=next_n)
     dm = DevMqa(inp)
     base, wb = host_out(dm.run())
     v = 0 if variant == "fp8" else 1

@@ -180,11 +180,13 @@ def test_largest_shape_and_batch():
     check_sampled(dm, dm.run(schedule=sched), np.random.default_rng(2), "schedule")
 
 
-def test_graph_replay_general_and_passes():
-    """A call with several slot passes (two launches of the general kernel)
-    captured once with its schedule; replays with new inputs match the
+@pytest.mark.parametrize("shape", [(96, 192, 3), (64, 128, 6)], ids=_id)
+def test_graph_replay_general_and_passes(shape):
+    """A call with several slot passes captured once with its schedule (96 x
+    192: three launches of the general kernel, one slot each; 64 x 128, six
+    slots: launches of 4 and 2 slots); replays with new inputs match the
     oracle."""
-    H, D, N = 96, 192, 3  # 32 KB budget / (2 planes x 96 x 128 B) = 1 slot per pass
+    H, D, N = shape
 
     def make(seed):
         lens = np.random.default_rng(seed).integers(0, 3000, 23)
