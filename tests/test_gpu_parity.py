@@ -463,3 +463,64 @@ def test_largest_batch():
     check_sampled(dm, dm.run(), np.random.default_rng(5), "in-call")
     sched = pm().mqa_logits_schedule(dm.sl, 1, 0, max_context=inp.max_context)
     check_sampled(dm, dm.run(schedule=sched), np.random.default_rng(6), "schedule")
+
+
+# ------------------------------------------------------- strided views
+
+
+@pytest.mark.parametrize("variant,H,D", [("fp8", 64, 128), ("mxfp4", 64, 128), ("fp8", 40, 80)],
+                         ids=["fp8", "mxfp4", "fp8_general"])
+def test_strided_output_and_block_table(variant, H, D):
+    """out rows wider than max_context (a view into a wider buffer) and a block
+    table that is a column slice of a wider table: values bit-identical to the
+    dense layouts, and the columns past max_context untouched."""
+    lens = np.random.default_rng(320).integers(0, 3000, 23)
+    lens[5] = 0
+    inp = synth.make_mqa_inputs(lens, 2, variant=variant, num_heads=H, head_dim=D,
+                                max_context=3072, bt_width=48, seed=320)
+    dm = DevMqa(inp)
+    ref, ref_wrote = host_out(dm.run())
+    m = pm()
+    out_dtype = torch.float32 if inp.out_dtype == "f32" else torch.bfloat16
+    wide = torch.empty((inp.rows, inp.max_context + 100), dtype=out_dtype, device=DEV)
+    if out_dtype == torch.float32:
+        wide.view(torch.int32).fill_(0x7FC0FFEE)
+    else:
+        wide.view(torch.int16).fill_(0x7FC1)
+    view = wide[:, : inp.max_context]
+    bt_wide = torch.full((inp.batch, 48 + 13), -1, dtype=torch.int32, device=DEV)
+    bt_wide[:, :48] = dm.bt
+    bt_view = bt_wide[:, :48]
+    if variant == "fp8":
+        m.mqa_logits_fp8(dm.q, dm.kv, dm.w, dm.sl, bt_view, max_context=inp.max_context, out=view)
+    else:
+        m.mqa_logits_mxfp4(dm.q, dm.q_sf, dm.kv, dm.w, dm.sl, bt_view,
+                           max_context=inp.max_context, out=view)
+    torch.cuda.synchronize()
+    got, wrote = host_out(view.contiguous())
+    assert np.array_equal(wrote, ref_wrote)
+    assert np.array_equal(got[wrote], ref[wrote])
+    tail = wide[:, inp.max_context:].contiguous().cpu()
+    if out_dtype == torch.float32:
+        assert (tail.view(torch.int32) == 0x7FC0FFEE).all()
+    else:
+        assert (tail.view(torch.int16) == 0x7FC1).all()
+
+
+def test_indexer_strided_scores_and_block_table():
+    ix = synth.make_config("indexer_bf16")
+    di = DevIndexer(ix)
+    ref, ref_wrote = host_out(di.run())
+    wide = torch.empty((ix.rows, ix.max_context + 64), dtype=torch.float32, device=DEV)
+    wide.view(torch.int32).fill_(0x7FC0FFEE)
+    view = wide[:, : ix.max_context]
+    W = di.bt.shape[1]
+    bt_wide = torch.full((di.bt.shape[0], W + 7), -1, dtype=torch.int32, device=DEV)
+    bt_wide[:, :W] = di.bt
+    pm().indexer_scores(di.q, di.kc, bt_wide[:, :W], di.lens, requests=di.reqs, scores=view,
+                        group_row_offsets=di.offs)
+    torch.cuda.synchronize()
+    got, wrote = host_out(view.contiguous())
+    assert np.array_equal(wrote, ref_wrote)
+    assert np.array_equal(got[wrote], ref[wrote])
+    assert (wide[:, ix.max_context:].contiguous().cpu().view(torch.int32) == 0x7FC0FFEE).all()
