@@ -38,6 +38,8 @@ METRIC_INDEXER = "KV positions/sec and achieved HBM GB/s, one-head bf16 indexer 
 METRIC_INDEXER_NVFP4 = ("KV positions/sec and achieved HBM GB/s, one-head nvfp4 indexer scores "
                         "d=128")
 HBM_PEAK_GBS = 8000.0
+# dense matrix peaks of MI355X, TFLOP/s
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "f16": 2500.0}
 MALL_BYTES = 256 << 20
 
 WORKLOADS = {
@@ -416,6 +418,12 @@ def main():
     # average over its launches (equal-size launches)
     achieved = positions * lbpp / (kern_avg * 1e-3) / 1e9
     value = positions * K / (total_ms * 1e-3)
+    # secondary roofline: the method's 2*H*D*next_n flops per KV position on
+    # the matrix cores, against the dense peak of the products' type
+    general = (inp.num_heads, inp.head_dim) != (64, 128)
+    mfma_type = "f16" if general else ("fp8" if inp.variant == "fp8" else "fp4")
+    flops = positions * 2.0 * inp.num_heads * inp.head_dim * inp.next_n
+    mfma_tflops = flops / (kern_avg * 1e-3) / 1e12
 
     line = {
         "metric": METRIC_FMT % (inp.variant, inp.num_heads, inp.head_dim),
@@ -450,6 +458,9 @@ def main():
             "launch_bytes_per_position": lbpp,
             "algorithmic_bytes_per_launch": positions * lbpp / len(slots),
             "counter_bytes_per_launch": traffic,
+            "mfma": {"achieved": mfma_tflops, "peak": MFMA_PEAK_TFLOPS[mfma_type],
+                     "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_PEAK_TFLOPS[mfma_type],
+                     "products": mfma_type, "flops_per_call": flops},
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
