@@ -199,12 +199,13 @@ int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t ro
  * Splits the (request, 64-token page) work items of one call, in request-major
  * order, into num_units contiguous ranges and writes the opaque int32 buffer
  * `schedule` of mqa_logits_schedule_ints(num_units) entries.  The ranges are
- * of near-equal length, except that with next_n >= 4 FP8 and the default unit
- * count the units of workgroups dispatched earlier on a compute unit get
- * proportionally more items (the same split the kernel makes by itself).  num_units in 1 .. 1<<20; 0 means mqa_logits_num_units(current
- * device, next_n, variant).  The result depends only on seq_lens, batch,
- * next_n, variant and max_context; it must be rebuilt whenever seq_lens
- * changes (including on every graph replay).
+ * of near-equal length, except that with FP8, next_n >= 4 and the default
+ * unit count the units of workgroups dispatched earlier on a compute unit get
+ * proportionally more items (the split the kernel makes by itself).
+ * num_units in 1 .. 1<<20; 0 means mqa_logits_num_units(current device,
+ * next_n, variant).  The result depends only on seq_lens, batch, next_n,
+ * variant and max_context; it must be rebuilt whenever seq_lens changes
+ * (including on every graph replay).  Any schedule gives the same logits.
  */
 int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,
                         int32_t max_context, int32_t num_units, int32_t* schedule, void* stream);
@@ -212,10 +213,12 @@ int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, 
 /* Number of int32 entries of a schedule buffer for num_units units. */
 int64_t mqa_logits_schedule_ints(int32_t num_units);
 
-/* The unit count a NULL-schedule call of this configuration uses on `device`:
- * the workgroups resident on the whole GPU, one contiguous range each (for a
- * batch with a short seq_lens prefix); < 0 on error.  A schedule built with
- * this count gives each workgroup one range, like the in-call split. */
+/* The unit count a NULL-schedule call with 64 heads and head_dim 128 uses on
+ * `device` for this next_n and variant: the workgroups of the call's first
+ * launch resident on the whole GPU, one contiguous range each; < 0 on error.
+ * A schedule built with this count gives each of them one range, like the
+ * in-call split (other shapes run another grid, which strides over the
+ * units). */
 int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant);
 
 /* Columns written per row for a request of seq_len tokens: ceil(seq_len/64)*64
