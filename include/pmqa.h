@@ -121,7 +121,12 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
  *   kv_fused     page i at kv_fused + i*page_stride; page_stride >= 4352, a
  *                multiple of 16.
  *   out_dtype    PMQA_BF16 (the default of this variant, round to nearest even)
- *                or PMQA_F32.
+ *                or PMQA_F32.  With PMQA_BF16 and a launch of two query slots
+ *                (next_n == 2, or the last pass of next_n == 6) the weighted
+ *                head sum runs on the matrix unit with each rectified score and
+ *                each weight rounded to bf16 once: at most 2^-8 * sum_h |w_h|
+ *                relu(q_h . k) of extra error before the output's own bf16
+ *                rounding.  PMQA_F32 output always sums at fp32 precision.
  *   Supported: num_heads == 64, head_dim == 128 (other values -> UNSUPPORTED),
  *   1 <= next_n <= 8 (next_n above 4 runs as two launches over the slots).
  *   Everything else as in mqa_logits_fp8.

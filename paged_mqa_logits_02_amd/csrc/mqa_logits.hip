@@ -384,9 +384,123 @@ __device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8
   if (NT == 2 || h == 0) store_logit<OUTT>(a.out, idx, v, valid);
 }
 
+// ------------------------------------------- head sum on the matrix unit
+
+// With bf16 output, the weighted head sum can run on the matrix unit: the
+// 16x16x128 products leave each lane 16 heads x 1 token (four head tiles), the
+// rectified scores are packed to bf16 and multiplied by the slot's weights (bf16,
+// row 0 of the A operand) with one 16x16x32 bf16 product per 32 heads.  This
+// replaces the rectifier-plus-FMA per score (two vector instructions) by one
+// vector instruction per score (half a conversion, half a packed max) and needs
+// no cross-lane reduction.  Each rectified score and each weight is rounded to
+// bf16 once (relative error <= 2^-9 each), so the head sum carries at most
+// 2^-8 * sum_h |w_h| relu(S_h) of extra error, which the bf16 output's own
+// rounding (2^-9) and tolerance absorb; fp32 output keeps the exact path.
+template <int N, int VAR, int OUTT> struct HeadSumOnMatrix {
+  static constexpr bool value = OUTT == 1 && VAR == 1 && N == 2;
+};
+
+// One slot of request b: the query's four head tiles (as QueryFrag) and the
+// head weights as bf16 A operands of the head reduction.  Reduction K step s
+// covers head tiles 2s and 2s+1; lane l (group g = l >> 4) holds K slots
+// 8g .. 8g+7, element e <-> head 32s + 16(e >> 2) + 4g + (e & 3), which is
+// where the first stage leaves that head's score in the B operand.  Only row 0
+// of A (lanes with (l & 15) == 0) carries weights; the other rows are zero.
+template <int VAR> struct RedQuery {
+  Frag<VAR> q[4];  // [head tile]
+  v4f wraw[2][2];  // [K step][head tile within the step]: weights as loaded
+  v8bf wa[2];      // [K step]: A operand
+};
+
+template <int VAR>
+__device__ __forceinline__ void settle_query(RedQuery<VAR>& qf) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    settle(qf.q[mt].v);
+    if constexpr (VAR == 1) settle(qf.q[mt].sf);
+  }
+  const bool row0 = (threadIdx.x & 15) == 0;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    settle(qf.wraw[st][0]);
+    settle(qf.wraw[st][1]);
+    v8bf w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (__bf16)(row0 ? qf.wraw[st][e >> 2][e & 3] : 0.0f);
+    qf.wa[st] = w;
+  }
+}
+
+template <int N, int VAR>
+__device__ __forceinline__ void load_query(RedQuery<VAR>& qf, const MqaArgs& a, int b, int t0,
+                                           int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  constexpr int kQRow = VAR == 0 ? 128 : 64;
+  const long long slot = row_of(a, b, t0);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const long long head_row = slot * 64 + 16 * mt + r;
+    qf.q[mt].load_global(a.q + head_row * kQRow, g);
+    if constexpr (VAR == 1) qf.q[mt].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      qf.wraw[st][hh] = __builtin_bit_cast(
+          v4f, ldg_untracked(a.w + slot * 64 + 32 * st + 16 * hh + 4 * g));
+}
+
+// Rectified bf16 pair: round to nearest even, then max with +0 as int16 (a
+// bf16 bit pattern with the sign bit set is a negative int16).
+__device__ __forceinline__ uint32_t relu_bf16x2(float x, float y) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2bf p = __builtin_convertvector((v2f){x, y}, v2bf);
+  const v2s m = __builtin_elementwise_max(__builtin_bit_cast(v2s, p), (v2s){0, 0});
+  return __builtin_bit_cast(uint32_t, m);
+}
+
+// Scores this wave's share of one staged page (one slot, SW 16-token
+// sub-tiles from s0) with the head sum on the matrix unit.
+template <int N, int VAR, int OUTT>
+__device__ __forceinline__ void score_page(const RedQuery<VAR>& qf, const uint8_t* stage,
+                                           const MqaArgs& a, int b, int j, bool valid, int t0,
+                                           int s0, int lane) {
+  constexpr int SW = WaveSplit<N>::SW;
+  const int g = lane >> 4, rr = lane & 15;
+  const long long row = row_of(a, b, t0) * a.out_row_stride + (long long)j * kPage;
+  Frag<VAR> kf[SW];
+#pragma unroll
+  for (int si = 0; si < SW; ++si) kf[si].load_stage(stage, 16 * (s0 + si) + rr, g);
+#pragma unroll
+  for (int si = 0; si < SW; ++si) {
+    v4f acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mma(qf.q[mt], kf[si]);
+    v4f r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const v4f& lo = acc[2 * st];
+      const v4f& hi = acc[2 * st + 1];
+      const uint32_t p0 = relu_bf16x2(lo[0], lo[1]), p1 = relu_bf16x2(lo[2], lo[3]);
+      const uint32_t p2 = relu_bf16x2(hi[0], hi[1]), p3 = relu_bf16x2(hi[2], hi[3]);
+      const v8bf kb = __builtin_bit_cast(v8bf, (v4i){(int)p0, (int)p1, (int)p2, (int)p3});
+      r = mfma_bf16(qf.wa[st], kb, r);
+    }
+    // row 0 of the result: lanes 0..15 hold tokens 16(s0+si) + 0..15
+    const int token = 16 * (s0 + si) + rr;
+    const float v = r[0] * stage_scale<VAR>(stage, token);
+    if (g == 0) store_logit<OUTT>(a.out, row + token, v, valid);
+  }
+}
+
 template <bool Wide, int N, int VAR> struct QueryPick { using type = QueryFrag<WaveSplit<N>::TW, VAR>; };
 template <int N, int VAR> struct QueryPick<true, N, VAR> { using type = WideQuery<VAR>; };
-template <int N, int VAR> struct QueryOf : QueryPick<WaveSplit<N>::kWide, N, VAR> {};
+template <int N, int VAR, int OUTT, bool Red = HeadSumOnMatrix<N, VAR, OUTT>::value>
+struct QueryOf : QueryPick<WaveSplit<N>::kWide, N, VAR> {};
+template <int N, int VAR, int OUTT> struct QueryOf<N, VAR, OUTT, true> { using type = RedQuery<VAR>; };
 
 template <int N, int VAR, typename Q>
 __device__ __forceinline__ void load_query_any(Q& qf, const MqaArgs& a, int b, int t0, int lane) {
@@ -458,7 +572,7 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
   // The first request's query slice is loaded before the first page loads
   // are issued, so that it is complete once page 0 is: the first wait is for
   // page 0, not for every page in flight.
-  typename QueryOf<N, VAR>::type qf;
+  typename QueryOf<N, VAR, OUTT>::type qf;
   load_query_any<N, VAR>(qf, a, b, t0, lane);
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) issue_next();

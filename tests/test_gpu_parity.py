@@ -126,6 +126,37 @@ def test_exact_arithmetic_bit_exact(variant, next_n):
     assert np.array_equal(gotb[written], refb)
 
 
+def test_mxfp4_bf16_head_sum_on_matrix_unit_exact():
+    """MXFP4 with bf16 output at next_n=2 sums the heads on the matrix unit:
+    every rectified score and weight is rounded to bf16 once before the sum.
+    With q, k in {0, +-1} and unit block scales every score is an integer of
+    magnitude <= 128 (exact in bf16) and the weights are powers of two, so the
+    result must equal the oracle's bf16 rounding bit for bit; the fp32 output
+    of the same inputs (exact path) must equal the oracle exactly."""
+    rng = np.random.default_rng(230)
+    inp = synth.make_mqa_inputs([300, 64, 1, 129, 0, 2000], 2, variant="mxfp4", max_context=2048,
+                                bt_width=32, seed=231)
+    grid = np.array([0.0, 1.0, -1.0], dtype=np.float32)
+    qf = rng.choice(grid, (inp.batch, 2, 64, 128)).astype(np.float32)
+    kf = rng.choice(grid, (inp.num_pages, 64, 128)).astype(np.float32)
+    inp.q, inp.q_sf = synth.quantize_mxfp4(qf)
+    inp.q_sf[:] = 127
+    packed, _ = synth.quantize_mxfp4(kf)
+    inp.kv[:, : 64 * 64] = packed.reshape(inp.num_pages, -1)
+    inp.kv[:, 64 * 64: 64 * 64 + 256] = 127
+    inp.weights[:] = rng.choice(np.array([0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32),
+                                inp.weights.shape)
+    ref, _, written = oracle.mqa_logits_for(inp)
+    say("mxfp4 N=2 bf16 head sum on the matrix unit, %d cells" % int(written.sum()))
+    dm = DevMqa(inp)
+    gotb, wroteb = host_out(dm.run(dtype=torch.bfloat16))
+    assert np.array_equal(wroteb, written)
+    refb = torch.from_numpy(ref[written]).float().bfloat16().double().numpy()
+    assert np.array_equal(gotb[written], refb)
+    got, _ = host_out(dm.run(dtype=torch.float32))
+    assert np.array_equal(got[written], ref[written])
+
+
 def test_one_head_fp8_equals_rectified_indexer_on_gpu():
     rng = np.random.default_rng(20)
     grid = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0])
