@@ -49,6 +49,9 @@ WORKLOADS = {
     "verify_fp8_n8": "B=64, next_n=8, H=64, d=128, page 64, seq_lens uniform 4K..64K, fp32 out",
     "verify_fp8_h32": "B=128, next_n=2, H=32, d=128, page 64, seq_lens uniform 4K..64K, "
                       "fp32 out",
+    "verify_fp8_bf16": "B=128, next_n=4, H=64, d=128, page 64, seq_lens uniform 4K..64K, "
+                       "bf16 out",
+    "mxfp4_n4": "B=64, next_n=4, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
     "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
     "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "

@@ -81,6 +81,12 @@ enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_MXFP4 = 1 };
  *                Only columns 0 .. seq_lens[b]-next_n+t of row b*next_n+t are
  *                meaningful; masking beyond that is the caller's job.
  *                max_context % 64 == 0, out_row_stride >= max_context.
+ *                PMQA_F32: the rectifier and the weighted head sum run in fp32.
+ *                PMQA_BF16 with 64 heads and head_dim 128: the weighted head sum
+ *                runs on the matrix unit in bf16 products (each rectified score
+ *                and each weight rounded to bf16 once, fp32 accumulation), at
+ *                most 2^-8 * sum_h |w_h| relu(q_h . k) (times s_p) of extra error
+ *                before the output's own bf16 rounding; other shapes sum in fp32.
  *   acc_dtype    PMQA_F32 (the only accumulator; anything else -> UNSUPPORTED).
  *                With 64 heads and head_dim 128 the products are FP8 matrix
  *                products, whose sums keep each product only down to 2^-13 of
@@ -121,12 +127,7 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
  *   kv_fused     page i at kv_fused + i*page_stride; page_stride >= 4352, a
  *                multiple of 16.
  *   out_dtype    PMQA_BF16 (the default of this variant, round to nearest even)
- *                or PMQA_F32.  With PMQA_BF16 and a launch of two query slots
- *                (next_n == 2, or the last pass of next_n == 6) the weighted
- *                head sum runs on the matrix unit with each rectified score and
- *                each weight rounded to bf16 once: at most 2^-8 * sum_h |w_h|
- *                relu(q_h . k) of extra error before the output's own bf16
- *                rounding.  PMQA_F32 output always sums at fp32 precision.
+ *                or PMQA_F32 (precision of each as in mqa_logits_fp8).
  *   Supported: num_heads == 64, head_dim == 128 (other values -> UNSUPPORTED),
  *   1 <= next_n <= 8 (next_n above 4 runs as two launches over the slots).
  *   Everything else as in mqa_logits_fp8.

@@ -386,113 +386,129 @@ __device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8
 
 // ------------------------------------------- head sum on the matrix unit
 
-// With bf16 output, the weighted head sum can run on the matrix unit: the
-// 16x16x128 products leave each lane 16 heads x 1 token (four head tiles), the
-// rectified scores are packed to bf16 and multiplied by the slot's weights (bf16,
-// row 0 of the A operand) with one 16x16x32 bf16 product per 32 heads.  This
-// replaces the rectifier-plus-FMA per score (two vector instructions) by one
-// vector instruction per score (half a conversion, half a packed max) and needs
-// no cross-lane reduction.  Each rectified score and each weight is rounded to
-// bf16 once (relative error <= 2^-9 each), so the head sum carries at most
+// With bf16 output the weighted head sum runs on the matrix unit.  The
+// 16x16x128 products leave each lane 16 heads x 1 token of a slot (four head
+// tiles); the rectified scores are packed to bf16 and multiplied by the
+// slot's weights (bf16) with 16x16x32 bf16 products.  Slot t's weights are
+// row t of the A operand and zero elsewhere, so the products of all of the
+// wave's slots accumulate into one result whose row t is slot t's logits
+// (lanes 0..15, element t).  One vector instruction per score (half a
+// conversion, half a packed max) instead of two, and no cross-lane
+// reduction.  Each rectified score and each weight is rounded to bf16 once
+// (relative error <= 2^-9 each), so the head sum carries at most
 // 2^-8 * sum_h |w_h| relu(S_h) of extra error, which the bf16 output's own
 // rounding (2^-9) and tolerance absorb; fp32 output keeps the exact path.
 template <int N, int VAR, int OUTT> struct HeadSumOnMatrix {
-  static constexpr bool value = OUTT == 1 && VAR == 1 && N == 2;
+  static constexpr bool value = OUTT == 1;
 };
 
-// One slot of request b: the query's four head tiles (as QueryFrag) and the
-// head weights as bf16 A operands of the head reduction.  Reduction K step s
-// covers head tiles 2s and 2s+1; lane l (group g = l >> 4) holds K slots
-// 8g .. 8g+7, element e <-> head 32s + 16(e >> 2) + 4g + (e & 3), which is
-// where the first stage leaves that head's score in the B operand.  Only row 0
-// of A (lanes with (l & 15) == 0) carries weights; the other rows are zero.
-template <int VAR> struct RedQuery {
-  Frag<VAR> q[4];  // [head tile]
-  v4f wraw[2][2];  // [K step][head tile within the step]: weights as loaded
-  v8bf wa[2];      // [K step]: A operand
+// The wave's TW slots of request b: each slot's query in four head tiles and
+// its head weights as bf16 A operands.  Reduction K step s covers head tiles
+// 2s and 2s+1; lane l (group g = l >> 4) holds K slots 8g .. 8g+7, element
+// e <-> head 32s + 16(e >> 2) + 4g + (e & 3), which is where the first stage
+// leaves that head's score in the B operand.
+template <int TW, int VAR> struct RedQuery {
+  Frag<VAR> q[4][TW];  // [head tile][slot]
+  v4f wraw[TW][2][2];  // [slot][K step][head tile within the step]: as loaded
+  v8bf wa[TW][2];      // [slot][K step]: A operand, nonzero in row `slot` only
 };
 
-template <int VAR>
-__device__ __forceinline__ void settle_query(RedQuery<VAR>& qf) {
+template <int TW, int VAR>
+__device__ __forceinline__ void settle_query(RedQuery<TW, VAR>& qf) {
+  const int row = threadIdx.x & 15;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    settle(qf.q[mt].v);
-    if constexpr (VAR == 1) settle(qf.q[mt].sf);
-  }
-  const bool row0 = (threadIdx.x & 15) == 0;
+  for (int t = 0; t < TW; ++t) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    settle(qf.wraw[st][0]);
-    settle(qf.wraw[st][1]);
-    v8bf w;
+    for (int mt = 0; mt < 4; ++mt) {
+      settle(qf.q[mt][t].v);
+      if constexpr (VAR == 1) settle(qf.q[mt][t].sf);
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = (__bf16)(row0 ? qf.wraw[st][e >> 2][e & 3] : 0.0f);
-    qf.wa[st] = w;
+    for (int st = 0; st < 2; ++st) {
+      settle(qf.wraw[t][st][0]);
+      settle(qf.wraw[t][st][1]);
+      v8bf w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = (__bf16)(row == t ? qf.wraw[t][st][e >> 2][e & 3] : 0.0f);
+      qf.wa[t][st] = w;
+    }
   }
 }
 
-template <int N, int VAR>
-__device__ __forceinline__ void load_query(RedQuery<VAR>& qf, const MqaArgs& a, int b, int t0,
-                                           int lane) {
+template <int N, int TW, int VAR>
+__device__ __forceinline__ void load_red_query(RedQuery<TW, VAR>& qf, const MqaArgs& a, int b,
+                                               int t0, int lane) {
   const int g = lane >> 4, r = lane & 15;
   constexpr int kQRow = VAR == 0 ? 128 : 64;
-  const long long slot = row_of(a, b, t0);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const long long head_row = slot * 64 + 16 * mt + r;
-    qf.q[mt].load_global(a.q + head_row * kQRow, g);
-    if constexpr (VAR == 1) qf.q[mt].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+  for (int t = 0; t < TW; ++t) {
+    const long long slot = row_of(a, b, t0 + t);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const long long head_row = slot * 64 + 16 * mt + r;
+      qf.q[mt][t].load_global(a.q + head_row * kQRow, g);
+      if constexpr (VAR == 1) qf.q[mt][t].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        qf.wraw[t][st][hh] = __builtin_bit_cast(
+            v4f, ldg_untracked(a.w + slot * 64 + 32 * st + 16 * hh + 4 * g));
   }
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      qf.wraw[st][hh] = __builtin_bit_cast(
-          v4f, ldg_untracked(a.w + slot * 64 + 32 * st + 16 * hh + 4 * g));
 }
 
 // Rectified bf16 pair: round to nearest even, then max with +0 as int16 (a
 // bf16 bit pattern with the sign bit set is a negative int16).
 __device__ __forceinline__ uint32_t relu_bf16x2(float x, float y) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
   typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
   typedef short v2s __attribute__((ext_vector_type(2)));
-  typedef float v2f __attribute__((ext_vector_type(2)));
   const v2bf p = __builtin_convertvector((v2f){x, y}, v2bf);
   const v2s m = __builtin_elementwise_max(__builtin_bit_cast(v2s, p), (v2s){0, 0});
   return __builtin_bit_cast(uint32_t, m);
 }
 
-// Scores this wave's share of one staged page (one slot, SW 16-token
+// Scores this wave's share of one staged page (TW slots, SW 16-token
 // sub-tiles from s0) with the head sum on the matrix unit.
-template <int N, int VAR, int OUTT>
-__device__ __forceinline__ void score_page(const RedQuery<VAR>& qf, const uint8_t* stage,
+template <int N, int VAR, int OUTT, int TW>
+__device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const uint8_t* stage,
                                            const MqaArgs& a, int b, int j, bool valid, int t0,
                                            int s0, int lane) {
   constexpr int SW = WaveSplit<N>::SW;
+  static_assert(TW == WaveSplit<N>::TW && TW <= 4, "one result row per slot");
   const int g = lane >> 4, rr = lane & 15;
-  const long long row = row_of(a, b, t0) * a.out_row_stride + (long long)j * kPage;
+  const long long col0 = (long long)j * kPage;
   Frag<VAR> kf[SW];
 #pragma unroll
   for (int si = 0; si < SW; ++si) kf[si].load_stage(stage, 16 * (s0 + si) + rr, g);
 #pragma unroll
   for (int si = 0; si < SW; ++si) {
-    v4f acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mma(qf.q[mt], kf[si]);
     v4f r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const v4f& lo = acc[2 * st];
-      const v4f& hi = acc[2 * st + 1];
-      const uint32_t p0 = relu_bf16x2(lo[0], lo[1]), p1 = relu_bf16x2(lo[2], lo[3]);
-      const uint32_t p2 = relu_bf16x2(hi[0], hi[1]), p3 = relu_bf16x2(hi[2], hi[3]);
-      const v8bf kb = __builtin_bit_cast(v8bf, (v4i){(int)p0, (int)p1, (int)p2, (int)p3});
-      r = mfma_bf16(qf.wa[st], kb, r);
+    for (int t = 0; t < TW; ++t) {
+      v4f acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = mma(qf.q[mt][t], kf[si]);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const v4f& lo = acc[2 * st];
+        const v4f& hi = acc[2 * st + 1];
+        const uint32_t p0 = relu_bf16x2(lo[0], lo[1]), p1 = relu_bf16x2(lo[2], lo[3]);
+        const uint32_t p2 = relu_bf16x2(hi[0], hi[1]), p3 = relu_bf16x2(hi[2], hi[3]);
+        const v8bf kb = __builtin_bit_cast(v8bf, (v4i){(int)p0, (int)p1, (int)p2, (int)p3});
+        r = mfma_bf16(qf.wa[t][st], kb, r);
+      }
     }
-    // row 0 of the result: lanes 0..15 hold tokens 16(s0+si) + 0..15
+    // lanes 0..15: element t = slot t's logit of token 16(s0+si) + (l & 15)
     const int token = 16 * (s0 + si) + rr;
-    const float v = r[0] * stage_scale<VAR>(stage, token);
-    if (g == 0) store_logit<OUTT>(a.out, row + token, v, valid);
+    const float sp = stage_scale<VAR>(stage, token);
+    if (g == 0) {
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + token,
+                          r[t] * sp, valid);
+    }
   }
 }
 
@@ -500,12 +516,23 @@ template <bool Wide, int N, int VAR> struct QueryPick { using type = QueryFrag<W
 template <int N, int VAR> struct QueryPick<true, N, VAR> { using type = WideQuery<VAR>; };
 template <int N, int VAR, int OUTT, bool Red = HeadSumOnMatrix<N, VAR, OUTT>::value>
 struct QueryOf : QueryPick<WaveSplit<N>::kWide, N, VAR> {};
-template <int N, int VAR, int OUTT> struct QueryOf<N, VAR, OUTT, true> { using type = RedQuery<VAR>; };
+template <int N, int VAR, int OUTT> struct QueryOf<N, VAR, OUTT, true> {
+  using type = RedQuery<WaveSplit<N>::TW, VAR>;
+};
 
 template <int N, int VAR, typename Q>
 __device__ __forceinline__ void load_query_any(Q& qf, const MqaArgs& a, int b, int t0, int lane) {
-  if constexpr (WaveSplit<N>::kWide) load_query<N, VAR>(qf, a, b, t0, lane);
-  else load_query<N, WaveSplit<N>::TW, VAR>(qf, a, b, t0, lane);
+  load_query<N, WaveSplit<N>::TW, VAR>(qf, a, b, t0, lane);
+}
+template <int N, int VAR>
+__device__ __forceinline__ void load_query_any(WideQuery<VAR>& qf, const MqaArgs& a, int b, int t0,
+                                               int lane) {
+  load_query<N, VAR>(qf, a, b, t0, lane);
+}
+template <int N, int VAR, int TW>
+__device__ __forceinline__ void load_query_any(RedQuery<TW, VAR>& qf, const MqaArgs& a, int b,
+                                               int t0, int lane) {
+  load_red_query<N, TW, VAR>(qf, a, b, t0, lane);
 }
 
 // Scores flat items f0 .. f0+count-1, the whole workgroup together.

@@ -345,18 +345,19 @@ def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=409
 # --------------------------------------------------------------------------
 
 SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5,
-         "indexer_nvfp4": 6, "verify_fp8_n8": 7, "verify_fp8_h32": 8}
+         "indexer_nvfp4": 6, "verify_fp8_n8": 7, "verify_fp8_h32": 8, "verify_fp8_bf16": 4,
+         "mxfp4_n4": 9}
 
 
 def _lens(name, rng):
     if name == "decode_fp8":
         u = rng.uniform(math.log(1024), math.log(32768), size=64)
         return np.rint(np.exp(u)).astype(np.int32)
-    if name in ("verify_fp8", "verify_fp8_h32"):
+    if name in ("verify_fp8", "verify_fp8_h32", "verify_fp8_bf16"):
         return rng.integers(4096, 65536 + 1, size=128).astype(np.int32)
     if name == "verify_fp8_n8":
         return rng.integers(4096, 65536 + 1, size=64).astype(np.int32)
-    if name == "mxfp4":
+    if name in ("mxfp4", "mxfp4_n4"):
         return rng.integers(16384, 131072 + 1, size=64).astype(np.int32)
     raise KeyError(name)
 
@@ -376,6 +377,8 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
     verify_fp8_n8  B=64, next_n=8, seq_lens uniform in 4K..64K, w ~ N(0, 0.1^2)
     verify_fp8_h32 B=128, next_n=2, 32 heads x 128, seq_lens uniform in 4K..64K,
                  w ~ N(0, 0.1^2)
+    verify_fp8_bf16 verify_fp8 (same seed and lengths) with bf16 out
+    mxfp4_n4     B=64, next_n=4, seq_lens uniform in 16K..128K, bf16 out
     """
     if seed is None:
         seed = SEEDS[name]
@@ -386,7 +389,8 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
         kw = dict(fmt="bf16" if name == "indexer_bf16" else "nvfp4")
         kw.update(overrides)
         return make_indexer_inputs(seed=seed, name=name, **kw)
-    elif name in ("decode_fp8", "verify_fp8", "mxfp4", "verify_fp8_n8", "verify_fp8_h32"):
+    elif name in ("decode_fp8", "verify_fp8", "mxfp4", "verify_fp8_n8", "verify_fp8_h32",
+                  "verify_fp8_bf16", "mxfp4_n4"):
         lens = _lens(name, np.random.default_rng(seed + 1000))
         if name == "decode_fp8":
             kw = dict(seq_lens=lens, next_n=1, max_context=32768, bt_width=512, w_std=0.1)
@@ -394,6 +398,12 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
             kw = dict(seq_lens=lens, next_n=4, max_context=65536, bt_width=1024, w_std=0.1)
         elif name == "verify_fp8_n8":
             kw = dict(seq_lens=lens, next_n=8, max_context=65536, bt_width=1024, w_std=0.1)
+        elif name == "verify_fp8_bf16":
+            kw = dict(seq_lens=lens, next_n=4, max_context=65536, bt_width=1024, w_std=0.1,
+                      out_dtype="bf16")
+        elif name == "mxfp4_n4":
+            kw = dict(seq_lens=lens, next_n=4, max_context=131072, bt_width=2048, w_std=1.0,
+                      variant="mxfp4")
         elif name == "verify_fp8_h32":
             kw = dict(seq_lens=lens, next_n=2, max_context=65536, bt_width=1024, w_std=0.1,
                       num_heads=32)

@@ -88,12 +88,12 @@ def test_ragged_batch(variant, next_n, dtype):
     check_dense(dm, dm.run(), "ragged %s N=%d %s" % (variant, next_n, dtype))
 
 
-def _exact_inputs(variant, next_n, seed):
+def _exact_inputs(variant, next_n, seed, grid=(0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0)):
     """Values on a coarse dyadic grid, so every partial sum is exact in fp32."""
     rng = np.random.default_rng(seed)
     inp = synth.make_mqa_inputs([300, 64, 1, 129], next_n, variant=variant, max_context=320,
                                 bt_width=5, seed=seed)
-    grid = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], dtype=np.float32)
+    grid = np.array(grid, dtype=np.float32)
     qf = rng.choice(grid, (inp.batch, next_n, 64, 128)).astype(np.float32)
     kf = rng.choice(grid, (inp.num_pages, 64, 128)).astype(np.float32)
     if variant == "fp8":
@@ -115,39 +115,29 @@ def _exact_inputs(variant, next_n, seed):
 @pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("next_n", [1, 4])
 def test_exact_arithmetic_bit_exact(variant, next_n):
+    """fp32 output: the rectifier and weighted head sum run in fp32, so on the
+    dyadic grid (partial sums exact in fp32) the result equals the oracle."""
     inp = _exact_inputs(variant, next_n, 200 + next_n)
     ref, _, written = oracle.mqa_logits_for(inp)
     dm = DevMqa(inp)
     got, wrote = host_out(dm.run(dtype=torch.float32))
     assert np.array_equal(wrote, written)
     assert np.array_equal(got[written], ref[written])
-    gotb, _ = host_out(dm.run(dtype=torch.bfloat16))
-    refb = torch.from_numpy(ref[written]).float().bfloat16().double().numpy()
-    assert np.array_equal(gotb[written], refb)
 
 
-def test_mxfp4_bf16_head_sum_on_matrix_unit_exact():
-    """MXFP4 with bf16 output at next_n=2 sums the heads on the matrix unit:
-    every rectified score and weight is rounded to bf16 once before the sum.
-    With q, k in {0, +-1} and unit block scales every score is an integer of
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("next_n", [1, 2, 3, 4, 6])
+def test_bf16_head_sum_on_matrix_unit_exact(variant, next_n):
+    """bf16 output sums the heads on the matrix unit: every rectified score and
+    weight is rounded to bf16 once before the sum.  With q, k in {0, +-1} (unit
+    block scales for MXFP4, s_p = 2^k for FP8) every score is an integer of
     magnitude <= 128 (exact in bf16) and the weights are powers of two, so the
     result must equal the oracle's bf16 rounding bit for bit; the fp32 output
-    of the same inputs (exact path) must equal the oracle exactly."""
-    rng = np.random.default_rng(230)
-    inp = synth.make_mqa_inputs([300, 64, 1, 129, 0, 2000], 2, variant="mxfp4", max_context=2048,
-                                bt_width=32, seed=231)
-    grid = np.array([0.0, 1.0, -1.0], dtype=np.float32)
-    qf = rng.choice(grid, (inp.batch, 2, 64, 128)).astype(np.float32)
-    kf = rng.choice(grid, (inp.num_pages, 64, 128)).astype(np.float32)
-    inp.q, inp.q_sf = synth.quantize_mxfp4(qf)
-    inp.q_sf[:] = 127
-    packed, _ = synth.quantize_mxfp4(kf)
-    inp.kv[:, : 64 * 64] = packed.reshape(inp.num_pages, -1)
-    inp.kv[:, 64 * 64: 64 * 64 + 256] = 127
-    inp.weights[:] = rng.choice(np.array([0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32),
-                                inp.weights.shape)
+    of the same inputs must equal the oracle exactly."""
+    inp = _exact_inputs(variant, next_n, 230 + next_n, grid=(0.0, 1.0, -1.0))
     ref, _, written = oracle.mqa_logits_for(inp)
-    say("mxfp4 N=2 bf16 head sum on the matrix unit, %d cells" % int(written.sum()))
+    say("%s N=%d bf16 head sum on the matrix unit, %d cells" % (variant, next_n,
+                                                                int(written.sum())))
     dm = DevMqa(inp)
     gotb, wroteb = host_out(dm.run(dtype=torch.bfloat16))
     assert np.array_equal(wroteb, written)
