@@ -482,9 +482,12 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
   Frag<VAR> kf[SW];
 #pragma unroll
   for (int si = 0; si < SW; ++si) kf[si].load_stage(stage, 16 * (s0 + si) + rr, g);
+  // All sub-tiles first (no store, hence no branch, in between, so the
+  // products of one sub-tile overlap the packing of the previous one).
+  v4f r[SW];
 #pragma unroll
   for (int si = 0; si < SW; ++si) {
-    v4f r = {0.f, 0.f, 0.f, 0.f};
+    r[si] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       v4f acc[4];
@@ -497,17 +500,31 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
         const uint32_t p0 = relu_bf16x2(lo[0], lo[1]), p1 = relu_bf16x2(lo[2], lo[3]);
         const uint32_t p2 = relu_bf16x2(hi[0], hi[1]), p3 = relu_bf16x2(hi[2], hi[3]);
         const v8bf kb = __builtin_bit_cast(v8bf, (v4i){(int)p0, (int)p1, (int)p2, (int)p3});
-        r = mfma_bf16(qf.wa[t][st], kb, r);
+        r[si] = mfma_bf16(qf.wa[t][st], kb, r[si]);
       }
     }
-    // lanes 0..15: element t = slot t's logit of token 16(s0+si) + (l & 15)
-    const int token = 16 * (s0 + si) + rr;
-    const float sp = stage_scale<VAR>(stage, token);
-    if (g == 0) {
+  }
+  // Row t of sub-tile si's result (lanes 0..15, element t) holds slot t's
+  // logits of tokens 16(s0+si) + 0..15.  The permlane swaps gather the
+  // sub-tiles into consecutive 16-lane rows: lane l then holds token 16 s0 + l.
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
-        store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + token,
-                          r[t] * sp, valid);
+  for (int t = 0; t < TW; ++t) {
+    const long long row = row_of(a, b, t0 + t) * a.out_row_stride + col0;
+    if constexpr (SW == 4) {
+      float x0 = r[0][t], x1 = r[1][t], x2 = r[2][t], x3 = r[3][t];
+      swap16(x0, x1);  // x0 rows: sub-tile 0, sub-tile 1, -, -
+      swap16(x2, x3);  // x2 rows: sub-tile 2, sub-tile 3, -, -
+      swap32(x0, x2);  // x0 rows: sub-tiles 0, 1, 2, 3
+      const int token = 16 * s0 + lane;
+      store_logit<OUTT>(a.out, row + token, x0 * stage_scale<VAR>(stage, token), valid);
+    } else if constexpr (SW == 2) {
+      float x0 = r[0][t], x1 = r[1][t];
+      swap16(x0, x1);  // x0 rows: sub-tile 0, sub-tile 1, -, -
+      const int token = 16 * s0 + lane;
+      if (lane < 32) store_logit<OUTT>(a.out, row + token, x0 * stage_scale<VAR>(stage, token), valid);
+    } else {
+      const int token = 16 * s0 + rr;
+      if (g == 0) store_logit<OUTT>(a.out, row + token, r[0][t] * stage_scale<VAR>(stage, token), valid);
     }
   }
 }
