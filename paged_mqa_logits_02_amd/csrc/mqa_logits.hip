@@ -458,6 +458,42 @@ __device__ __forceinline__ void load_red_query(RedQuery<TW, VAR>& qf, const MqaA
   }
 }
 
+// Key fragment of sub-tile s (rows 16s .. 16s+15) of a staged page.  Row
+// 16s + rr has the same XOR swizzle as row rr (the swizzle reads bits 1..3
+// of the row), so a lane's byte offset is the same in every sub-tile and the
+// sub-tile adds a constant that folds into the LDS read's offset field.
+__device__ __forceinline__ void load_subtile(Frag<0>& f, const uint8_t* stage, int s, int rr,
+                                             int g) {
+  using L = PageLayout<0>;
+  const int sw = L::swz(rr);
+  const uint8_t* row = stage + (16 * s + rr) * L::kRowBytes;
+  const v4i lo = *reinterpret_cast<const v4i*>(row + 16 * (g ^ sw));
+  const v4i hi = *reinterpret_cast<const v4i*>(row + 16 * ((4 + g) ^ sw));
+  f.v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// MXFP4: the lane's key and scale addresses of sub-tile 0 (rows from
+// 16 s0), computed once per page; sub-tile s adds s * 1024 / s * 64.  The
+// empty asm makes the two bases opaque, so the compiler keeps them as bases
+// with the sub-tile constant in the offset field (rather than hoisting one
+// lane offset per sub-tile and adding the page base to each).
+struct Fp4SubtileBase {
+  typedef __attribute__((address_space(3))) const uint8_t* lds_ptr;
+  lds_ptr key, scale;
+  __device__ __forceinline__ Fp4SubtileBase(const uint8_t* stage, int s0, int rr, int g) {
+    using L = PageLayout<1>;
+    const lds_ptr st = (lds_ptr)stage;
+    key = st + (16 * s0 + rr) * L::kRowBytes + 16 * (g ^ L::swz(rr));
+    scale = st + L::kKeyBytes + (16 * s0 + rr) * 4 + g;
+    asm("" : "+v"(key));
+    asm("" : "+v"(scale));
+  }
+  __device__ __forceinline__ void load(Frag<1>& f, int s) const {
+    f.v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+        key + 16 * s * PageLayout<1>::kRowBytes);
+    f.sf = scale[16 * s * 4];
+  }
+};
+
 // Rectified bf16 pair: round to nearest even, then max with +0 as int16 (a
 // bf16 bit pattern with the sign bit set is a negative int16).
 __device__ __forceinline__ uint32_t relu_bf16x2(float x, float y) {
@@ -480,8 +516,14 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
   const int g = lane >> 4, rr = lane & 15;
   const long long col0 = (long long)j * kPage;
   Frag<VAR> kf[SW];
+  if constexpr (VAR == 1) {
+    const Fp4SubtileBase base(stage, s0, rr, g);
 #pragma unroll
-  for (int si = 0; si < SW; ++si) kf[si].load_stage(stage, 16 * (s0 + si) + rr, g);
+    for (int si = 0; si < SW; ++si) base.load(kf[si], si);
+  } else {
+#pragma unroll
+    for (int si = 0; si < SW; ++si) load_subtile(kf[si], stage, s0 + si, rr, g);
+  }
   // All sub-tiles first (no store, hence no branch, in between, so the
   // products of one sub-tile overlap the packing of the previous one).
   v4f r[SW];
