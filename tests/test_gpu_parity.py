@@ -255,8 +255,9 @@ def test_indexer_nvfp4_out_of_range_page_is_nan():
 # ------------------------------------------------------- full-size configs
 
 
-@pytest.mark.parametrize("name", ["decode_fp8", "verify_fp8", "mxfp4"])
-@pytest.mark.parametrize("mode", ["in_call", "schedule"])
+@pytest.mark.parametrize("name,mode", [
+    (n, m) for n in ("decode_fp8", "verify_fp8", "mxfp4") for m in ("in_call", "schedule")
+] + [("verify_fp8_bf16", "in_call"), ("mxfp4_n4", "in_call")])
 def test_full_size_config(name, mode):
     inp = synth.make_config(name)
     say("%s %s: B=%d N=%d pages=%d positions=%d" % (name, mode, inp.batch, inp.next_n,
