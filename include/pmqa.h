@@ -151,8 +151,9 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
  *   block_table      int32 [num_requests, bt_stride], bt_width usable entries per
  *                    row, bt_width*64 >= max_context.
  *   context_lengths  int32 [groups]: keys of each group.
- *   requests         int32 [groups]: the block-table row of each group; not read
- *                    for a group of length <= 0, so any value is allowed there.
+ *   requests         int32 [groups]: the block-table row of each group; its value
+ *                    is not used for a group of length <= 0, so any value is
+ *                    allowed there (nothing is looked up with it).
  *   group_row_offsets  NULL: every group has rows/groups consecutive rows (an
  *                    integer in 1..8).  Otherwise int32 [groups+1], nondecreasing
  *                    from 0 to rows, each group 1..8 rows (device data: the host

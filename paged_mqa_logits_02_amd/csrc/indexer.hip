@@ -14,52 +14,31 @@
 
 namespace pmqa {
 
-__global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
-  const int g = blockIdx.y;
-  const int pi = blockIdx.x;
-  const int lane = threadIdx.x;
-  int L = a.lens[g];
-  L = L < a.max_context ? L : a.max_context;
-  if (L <= pi * kPage) return;  // also every group of length <= 0
-
-  int r0, G;
+// The group of wave (g, page pi): length, first row, row count and block-table
+// row, read together (one round trip; every read is in bounds for g < groups,
+// and the request is used only after the length check, so a length-0 group's
+// request may hold any value).  Returns false if the wave has nothing to do.
+struct GroupMeta {
+  int L, r0, G, req;
+};
+__device__ __forceinline__ bool group_meta(const IdxArgs& a, int g, int pi, GroupMeta& m) {
+  const int L = a.lens[g];
+  m.req = a.reqs[g];
+  int r0 = g * a.uniform_g, r1 = r0 + a.uniform_g;
   if (a.offs) {
     r0 = a.offs[g];
-    G = a.offs[g + 1] - r0;
-  } else {
-    r0 = g * a.uniform_g;
-    G = a.uniform_g;
+    r1 = a.offs[g + 1];
   }
-  if (G < 1 || G > 8 || r0 < 0 || r0 + G > a.rows) return;
+  m.L = L < a.max_context ? L : a.max_context;
+  m.r0 = r0;
+  m.G = r1 - r0;
+  if (m.L <= pi * kPage) return false;  // also every group of length <= 0
+  return m.G >= 1 && m.G <= 8 && r0 >= 0 && r0 + m.G <= a.rows;
+}
 
-  const int req = a.reqs[g];
-  bool bad = (unsigned)req >= (unsigned)a.num_requests;
-  int pg = bad ? 0 : a.bt[(long long)req * a.bt_stride + pi];
-  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
-
+__device__ __forceinline__ void store_scores(const IdxArgs& a, const GroupMeta& m, int pi,
+                                             int lane, bool bad, const v4f (&acc)[4]) {
   const int kg = lane >> 4, r = lane & 15;
-  // A: row r of the group, d in [32ks + 8kg, 32ks + 8kg + 8)
-  v8bf qa[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (r < G) qa[ks] = ldg<v8bf>(a.q + (long long)(r0 + r) * 128 + 32 * ks + 8 * kg);
-    else qa[ks] = (v8bf){};
-  }
-
-  const uint8_t* page = a.kc + (long long)pg * a.page_stride;
-  v4f acc[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
-    if (!bad) {
-      const uint16_t* key = reinterpret_cast<const uint16_t*>(page) + (16 * s + r) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v8bf kb = ldg_stream<v8bf>(key + 32 * ks + 8 * kg);
-        acc[s] = mfma_bf16(qa[ks], kb, acc[s]);
-      }
-    }
-  }
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -67,9 +46,55 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * kg + i;
-      if (row < G && col < L) a.scores[(long long)(r0 + row) * a.srs + col] = bad ? nan : acc[s][i];
+      if (row < m.G && col < m.L)
+        a.scores[(long long)(m.r0 + row) * a.srs + col] = bad ? nan : acc[s][i];
     }
   }
+}
+
+__global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
+  const int g = blockIdx.y;
+  const int pi = blockIdx.x;
+  const int lane = threadIdx.x;
+  GroupMeta m;
+  if (!group_meta(a, g, pi, m)) return;
+
+  bool bad = (unsigned)m.req >= (unsigned)a.num_requests;
+  const int pg = bad ? 0 : a.bt[(long long)m.req * a.bt_stride + pi];
+
+  // A: row r of the group, d in [32ks + 8kg, 32ks + 8kg + 8); lanes past the
+  // group's rows load its first row (so every load is issued at once, while
+  // the block-table entry is in flight) and use zeros.
+  const int kg = lane >> 4, r = lane & 15;
+  const long long qrow = m.r0 + (r < m.G ? r : 0);
+  v8bf qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = ldg<v8bf>(a.q + qrow * 128 + 32 * ks + 8 * kg);
+
+  // B: all four 16-token tiles of the page at once; an out-of-range page id
+  // reads page 0 instead and its scores are written as NaN.
+  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
+  const uint16_t* keys =
+      reinterpret_cast<const uint16_t*>(a.kc + (long long)(bad ? 0 : pg) * a.page_stride);
+  v8bf kb[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kb[s][ks] = ldg_stream<v8bf>(keys + (16 * s + r) * 128 + 32 * ks + 8 * kg);
+
+  if (r >= m.G) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8bf){};
+  }
+  v4f acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[s][ks], acc[s]);
+  }
+  store_scores(a, m, pi, lane, bad, acc);
 }
 
 // ------------------------------------------------------------------ NVFP4
@@ -120,64 +145,50 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
   const int g = blockIdx.y;
   const int pi = blockIdx.x;
   const int lane = threadIdx.x;
-  int L = a.lens[g];
-  L = L < a.max_context ? L : a.max_context;
-  if (L <= pi * kPage) return;  // also every group of length <= 0
+  GroupMeta m;
+  if (!group_meta(a, g, pi, m)) return;
 
-  int r0, G;
-  if (a.offs) {
-    r0 = a.offs[g];
-    G = a.offs[g + 1] - r0;
-  } else {
-    r0 = g * a.uniform_g;
-    G = a.uniform_g;
-  }
-  if (G < 1 || G > 8 || r0 < 0 || r0 + G > a.rows) return;
+  bool bad = (unsigned)m.req >= (unsigned)a.num_requests;
+  const int pg = bad ? 0 : a.bt[(long long)m.req * a.bt_stride + pi];
 
-  const int req = a.reqs[g];
-  bool bad = (unsigned)req >= (unsigned)a.num_requests;
-  int pg = bad ? 0 : a.bt[(long long)req * a.bt_stride + pi];
-  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
-
+  // The query row (lanes past the group's rows read its first row and use
+  // zeros) and, once the page id is known, all four key tiles, each load
+  // issued before any is waited for.
   const int kg = lane >> 4, r = lane & 15;
   const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
+  const long long qrow = m.r0 + (r < m.G ? r : 0);
+  const v4i qpacked = ldg<v4i>(q8 + qrow * 64 + 16 * kg);
+  const uint32_t qsc = *reinterpret_cast<const uint16_t*>(a.qs + qrow * 8 + 2 * kg);
+
+  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
+  const long long page_id = bad ? 0 : pg;
+  const uint8_t* page = a.kc + page_id * a.page_stride;
+  const uint8_t* pscale = a.ks + page_id * a.scale_page_stride;
+  v4i kpacked[4];
+  uint32_t ksc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int key = 16 * s + r;
+    kpacked[s] = ldg_stream<v4i>(page + key * 64 + 16 * kg);
+    ksc[s] = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
+  }
+
   v8bf qa[4];
-  if (r < G) {
-    const long long row = r0 + r;
-    const v4i packed = ldg<v4i>(q8 + row * 64 + 16 * kg);
-    const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.qs + row * 8 + 2 * kg);
-    dequant_row(packed, sc, qa);
-  } else {
+  dequant_row(qpacked, qsc, qa);
+  if (r >= m.G) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8bf){};
   }
-
-  const uint8_t* page = a.kc + (long long)pg * a.page_stride;
-  const uint8_t* pscale = a.ks + (long long)pg * a.scale_page_stride;
   v4f acc[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
+    v8bf kb[4];
+    dequant_row(kpacked[s], ksc[s], kb);
     acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
-    if (!bad) {
-      const int key = 16 * s + r;
-      const v4i packed = ldg_stream<v4i>(page + key * 64 + 16 * kg);
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
-      v8bf kb[4];
-      dequant_row(packed, sc, kb);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
-    }
+    for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
   }
-  const float nan = __builtin_nanf("");
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int col = pi * kPage + 16 * s + r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kg + i;
-      if (row < G && col < L) a.scores[(long long)(r0 + row) * a.srs + col] = bad ? nan : acc[s][i];
-    }
-  }
+  store_scores(a, m, pi, lane, bad, acc);
 }
 
 hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream) {
