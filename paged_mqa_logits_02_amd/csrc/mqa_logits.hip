@@ -730,10 +730,15 @@ __global__ void __launch_bounds__(256) PMQA_OCCUPANCY
   const int G = gridDim.x;
   const int unit = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
+  // The schedule header is read at once (no short-circuit between its
+  // fields, which would make each read wait for the previous one).
   const int32_t* sc = a.schedule;
-  const bool use_sched = sc != nullptr && sc[0] == kSchedMagic && sc[2] == a.next_n &&
-                         sc[3] == VAR && sc[4] == a.max_context && sc[5] == a.batch &&
-                         sc[1] > 0;
+  bool use_sched = false;
+  if (sc != nullptr) {
+    const int h0 = sc[0], h1 = sc[1], h2 = sc[2], h3 = sc[3], h4 = sc[4], h5 = sc[5];
+    use_sched = (h0 == kSchedMagic) & (h2 == a.next_n) & (h3 == VAR) & (h4 == a.max_context) &
+                (h5 == a.batch) & (h1 > 0);
+  }
   if (use_sched) {
     // Units come from the schedule's split points (flat item indices); the
     // request and page of each item are re-derived from the current seq_lens,
