@@ -147,6 +147,35 @@ def test_bf16_head_sum_on_matrix_unit_exact(variant, next_n):
     assert np.array_equal(got[written], ref[written])
 
 
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("next_n", [1, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_extreme_magnitudes(variant, next_n, dtype):
+    """Scores far from 1: FP8 q and k at +-448 (|q.k| up to 128 * 448^2, about
+    2.6e7) with large and tiny weights; MXFP4 with e8m0 block scales from 2^-20
+    to 2^20 (scores up to ~2^45).  Both output paths (the fp32 epilogue and the
+    bf16 head sum) must stay within the tolerance without overflow."""
+    rng = np.random.default_rng(240 + next_n)
+    inp = synth.make_mqa_inputs([300, 64, 1, 129], next_n, variant=variant, max_context=320,
+                                bt_width=5, seed=241 + next_n, out_dtype=dtype)
+    if variant == "fp8":
+        sign = lambda shape: np.where(rng.random(shape) < 0.5, -448.0, 448.0)  # noqa: E731
+        qf = sign((inp.batch, next_n, 64, 128)) * (rng.random((inp.batch, next_n, 64, 128)) < 0.9)
+        kf = sign((inp.num_pages, 64, 128))
+        inp.q = synth.encode_e4m3(qf.astype(np.float32))
+        inp.kv[:, : 64 * 128] = synth.encode_e4m3(kf.astype(np.float32)).reshape(inp.num_pages, -1)
+    else:
+        inp.q_sf[:] = rng.integers(127 - 20, 127 + 21, inp.q_sf.shape).astype(np.uint8)
+        sf = rng.integers(127 - 20, 127 + 21, (inp.num_pages, 64, 4)).astype(np.uint8)
+        inp.kv[:, 64 * 64: 64 * 64 + 256] = sf.reshape(inp.num_pages, -1)
+    w = rng.standard_normal(inp.weights.shape).astype(np.float32)
+    w *= np.ldexp(1.0, rng.integers(-12, 13, w.shape)).astype(np.float32)
+    inp.weights[:] = w
+    say("extreme magnitudes %s N=%d %s" % (variant, next_n, dtype))
+    dm = DevMqa(inp)
+    check_dense(dm, dm.run(), "extreme %s N=%d %s" % (variant, next_n, dtype))
+
+
 def test_one_head_fp8_equals_rectified_indexer_on_gpu():
     rng = np.random.default_rng(20)
     grid = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0])
