@@ -119,44 +119,55 @@ __device__ void load_slice(const MqaArgs& a, int b, uint8_t* q_lds, float* w_lds
   if (in_slice) w_lds[e] = real ? wv : 0.0f;
 }
 
-// Scores tokens 16*wave .. 16*wave+15 of one staged page for every slot of
-// the launch and stores them.  A plane's 32 bytes per lane (Frag<0>) feed four
-// f16 products of 8 values each, in the same order for query and key.
-template <int KS, int OUTT>
-__device__ __forceinline__ void score_page_any(const uint8_t* stage, const uint8_t* q_lds,
-                                               const float* w_lds, const MqaArgs& a, int b, int j,
-                                               bool valid, int Hp, int wave, int lane,
-                                               bool partial, bool lo_ok, bool hi_ok,
-                                               bool hi_any) {
+// Scores tokens 16*wave .. 16*wave+15 of NP consecutive staged pages of one
+// request (NP = 1 or 2) for every slot of the launch and stores them.  A
+// plane's 32 bytes per lane (Frag<0>) feed four f16 products of 8 values
+// each, in the same order for query and key.  With two pages each query
+// fragment is read from LDS and widened to f16 once for both pages.
+template <int KS, int OUTT, int NP>
+__device__ __forceinline__ void score_pages_any(const uint8_t* const (&stage)[NP],
+                                                const uint8_t* q_lds, const float* w_lds,
+                                                const MqaArgs& a, int b, int j0,
+                                                const bool (&valid)[NP], int Hp, int wave,
+                                                int lane, bool partial, bool lo_ok, bool hi_ok,
+                                                bool hi_any) {
   const int g = lane >> 4, rr = lane & 15;
   const int r = 16 * wave + rr;  // key row = token of the page
-  Frag<0> kf[KS];
+  v8h kh[NP][KS][4];
+  float sp[NP];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kf[ks].load_stage(stage + ks * kPlaneBytes, r, g);
-  if (partial) {
-    // the lane's two chunks of the last plane: d in [16c, 16c+16) for
-    // c = 8(KS-1)+g (elements 0-3) and c = 8(KS-1)+4+g (elements 4-7)
+  for (int p = 0; p < NP; ++p) {
+    Frag<0> kf[KS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kf[KS - 1].v[i] = lo_ok ? kf[KS - 1].v[i] : 0;
-      kf[KS - 1].v[4 + i] = hi_ok ? kf[KS - 1].v[4 + i] : 0;
+    for (int ks = 0; ks < KS; ++ks) kf[ks].load_stage(stage[p] + ks * kPlaneBytes, r, g);
+    if (partial) {
+      // the lane's two chunks of the last plane: d in [16c, 16c+16) for
+      // c = 8(KS-1)+g (elements 0-3) and c = 8(KS-1)+4+g (elements 4-7)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kf[KS - 1].v[i] = lo_ok ? kf[KS - 1].v[i] : 0;
+        kf[KS - 1].v[4 + i] = hi_ok ? kf[KS - 1].v[4 + i] : 0;
+      }
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kh[p][ks][u] = e4m3x8_to_f16(kf[ks].v[2 * u], kf[ks].v[2 * u + 1]);
+    sp[p] = *reinterpret_cast<const float*>(stage[p] + PlaneLayout<KS>::kKeyBytes + 4 * r);
   }
-  v8h kh[KS][4];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kh[ks][u] = e4m3x8_to_f16(kf[ks].v[2 * u], kf[ks].v[2 * u + 1]);
-  const float sp = *reinterpret_cast<const float*>(stage + PlaneLayout<KS>::kKeyBytes + 4 * r);
-  const long long col = (long long)j * kPage + r;
   const int slice = KS * Hp * 128;
   for (int t = 0; t < a.slots; ++t) {
     const uint8_t* qt = q_lds + t * slice;
     const float* wt = w_lds + t * Hp;
-    float s_even = 0.0f, s_odd = 0.0f;
+    float s_even[NP], s_odd[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) s_even[p] = s_odd[p] = 0.0f;
     // two 16-head tiles per step (Hp is a multiple of 32)
     for (int h0 = 0; h0 < Hp; h0 += 32) {
-      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      v4f acc0[NP], acc1[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) acc0[p] = acc1[p] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         Frag<0> q0, q1;
@@ -166,24 +177,39 @@ __device__ __forceinline__ void score_page_any(const uint8_t* stage, const uint8
         for (int u = 0; u < 4; ++u) {
           // the second half of the last plane is all zero when D ends in its first half
           if (u >= 2 && ks == KS - 1 && !hi_any) continue;
-          acc0 = mfma_f16(e4m3x8_to_f16(q0.v[2 * u], q0.v[2 * u + 1]), kh[ks][u], acc0);
-          acc1 = mfma_f16(e4m3x8_to_f16(q1.v[2 * u], q1.v[2 * u + 1]), kh[ks][u], acc1);
+          const v8h qa0 = e4m3x8_to_f16(q0.v[2 * u], q0.v[2 * u + 1]);
+          const v8h qa1 = e4m3x8_to_f16(q1.v[2 * u], q1.v[2 * u + 1]);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            acc0[p] = mfma_f16(qa0, kh[p][ks][u], acc0[p]);
+            acc1[p] = mfma_f16(qa1, kh[p][ks][u], acc1[p]);
+          }
         }
       }
       // lane l holds heads h0 + 4g + i (tile 0) and h0 + 16 + 4g + i (tile 1)
       const v4f w0 = *reinterpret_cast<const v4f*>(wt + h0 + 4 * g);
       const v4f w1 = *reinterpret_cast<const v4f*>(wt + h0 + 16 + 4 * g);
-      s_even = __builtin_fmaf(w0[0], relu(acc0[0]), s_even);
-      s_odd = __builtin_fmaf(w0[1], relu(acc0[1]), s_odd);
-      s_even = __builtin_fmaf(w0[2], relu(acc0[2]), s_even);
-      s_odd = __builtin_fmaf(w0[3], relu(acc0[3]), s_odd);
-      s_even = __builtin_fmaf(w1[0], relu(acc1[0]), s_even);
-      s_odd = __builtin_fmaf(w1[1], relu(acc1[1]), s_odd);
-      s_even = __builtin_fmaf(w1[2], relu(acc1[2]), s_even);
-      s_odd = __builtin_fmaf(w1[3], relu(acc1[3]), s_odd);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        s_even[p] = __builtin_fmaf(w0[0], relu(acc0[p][0]), s_even[p]);
+        s_odd[p] = __builtin_fmaf(w0[1], relu(acc0[p][1]), s_odd[p]);
+        s_even[p] = __builtin_fmaf(w0[2], relu(acc0[p][2]), s_even[p]);
+        s_odd[p] = __builtin_fmaf(w0[3], relu(acc0[p][3]), s_odd[p]);
+        s_even[p] = __builtin_fmaf(w1[0], relu(acc1[p][0]), s_even[p]);
+        s_odd[p] = __builtin_fmaf(w1[1], relu(acc1[p][1]), s_odd[p]);
+        s_even[p] = __builtin_fmaf(w1[2], relu(acc1[p][2]), s_even[p]);
+        s_odd[p] = __builtin_fmaf(w1[3], relu(acc1[p][3]), s_odd[p]);
+      }
     }
-    const float v = row_reduce4(s_even + s_odd) * sp;
-    if (g == 0) store_logit<OUTT>(a.out, row_of(a, b, t) * a.out_row_stride + col, v, valid);
+    float v[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) v[p] = row_reduce4(s_even[p] + s_odd[p]) * sp[p];
+    if (g == 0) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        store_logit<OUTT>(a.out, row_of(a, b, t) * a.out_row_stride + (long long)(j0 + p) * kPage + r,
+                          v[p], valid[p]);
+    }
   }
 }
 
@@ -195,7 +221,10 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
                                   uint8_t* ring, uint8_t* q_lds, float* w_lds, long long f0,
                                   int count) {
   using L = PlaneLayout<KS>;
-  constexpr int kAhead = kStages - 1;
+  // Pages are scored in pairs, so a pair's two ring slots are in use while
+  // the next two pages load: kStages - 2 pages ahead.
+  constexpr int kAhead = kStages - 2;
+  static_assert(kAhead >= 1, "ring too short");
   const int B = a.batch;
   const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int Hp = heads_padded(a.heads);
@@ -248,12 +277,31 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
     load_slice<KS>(a, b, q_lds, w_lds, Hp, wave, lane);
     ring_barrier();  // the whole slice has landed
     const int pages = min(count - n, tiles_at(s_prefix, b) - j);
-    for (int k = 0; k < pages; ++k, ++n, ++j) {
+    // Pairs of pages, then a last single page.  Before a pair (n, n+1) the
+    // pages up to n + kAhead - 1 are issued; the pair issues two more, into
+    // the slots of pages n - 2 and n - 1, which this wave has scored (it
+    // reads only the rows it loaded, so program order is enough).
+    int k = 0;
+    for (; k + 1 < pages; k += 2, n += 2, j += 2) {
+      issue_next();
+      issue_next();
+      wait_page<L::kLoadsPerWave, kAhead>(issued - (n + 1) - 1);  // pages n and n+1
+      const uint8_t* const st[2] = {ring + ((unsigned)n % kStages) * L::kStageBytes,
+                                    ring + ((unsigned)(n + 1) % kStages) * L::kStageBytes};
+      const bool valid[2] = {((valid_bits >> (n & 31)) & 1u) != 0,
+                             ((valid_bits >> ((n + 1) & 31)) & 1u) != 0};
+      score_pages_any<KS, OUTT, 2>(st, q_lds, w_lds, a, b, j, valid, Hp, wave, lane, partial,
+                                   lo_ok, hi_ok, hi_any);
+    }
+    if (k < pages) {
       issue_next();
       wait_page<L::kLoadsPerWave, kAhead>(issued - n - 1);
-      const bool valid = (valid_bits >> (n & 31)) & 1u;
-      score_page_any<KS, OUTT>(ring + ((unsigned)n % kStages) * L::kStageBytes, q_lds, w_lds, a,
-                               b, j, valid, Hp, wave, lane, partial, lo_ok, hi_ok, hi_any);
+      const uint8_t* const st[1] = {ring + ((unsigned)n % kStages) * L::kStageBytes};
+      const bool valid[1] = {((valid_bits >> (n & 31)) & 1u) != 0};
+      score_pages_any<KS, OUTT, 1>(st, q_lds, w_lds, a, b, j, valid, Hp, wave, lane, partial,
+                                   lo_ok, hi_ok, hi_any);
+      ++n;
+      ++j;
     }
     ++b;
     j = 0;
@@ -289,9 +337,14 @@ __global__ void __launch_bounds__(256)
 
   const int G = gridDim.x;
   const int unit = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  // The schedule header is read at once (no short-circuit between its fields).
   const int32_t* sc = a.schedule;
-  const bool use_sched = sc != nullptr && sc[0] == kSchedMagic && sc[2] == a.next_n &&
-                         sc[3] == 0 && sc[4] == a.max_context && sc[5] == a.batch && sc[1] > 0;
+  bool use_sched = false;
+  if (sc != nullptr) {
+    const int h0 = sc[0], h1 = sc[1], h2 = sc[2], h3 = sc[3], h4 = sc[4], h5 = sc[5];
+    use_sched = (h0 == kSchedMagic) & (h2 == a.next_n) & (h3 == 0) & (h4 == a.max_context) &
+                (h5 == a.batch) & (h1 > 0);
+  }
   if (use_sched) {
     const int U = sc[1];
     for (int u = unit; u < U; u += G) {
