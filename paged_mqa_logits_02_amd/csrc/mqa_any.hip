@@ -37,6 +37,10 @@
 namespace pmqa {
 
 constexpr int kPlaneBytes = kPage * 128;  // a 128-byte plane of a page's 64 key rows
+#ifndef PMQA_ANY_STAGES
+#define PMQA_ANY_STAGES kStages
+#endif
+constexpr int kAnyStages = PMQA_ANY_STAGES;  // page ring slots of this kernel
 
 __host__ __device__ constexpr int heads_padded(int h) { return (h + 31) / 32 * 32; }
 
@@ -215,15 +219,15 @@ __device__ __forceinline__ void score_pages_any(const uint8_t* const (&stage)[NP
 
 // Scores flat items f0 .. f0+count-1, the whole workgroup together.  Page
 // pipeline as in the 64-head kernels when each wave scores only the rows it
-// loaded: kStages-1 pages in flight, no barrier per page.
+// loaded: no barrier per page.
 template <int KS, int OUTT>
 __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_pid,
                                   uint8_t* ring, uint8_t* q_lds, float* w_lds, long long f0,
                                   int count) {
   using L = PlaneLayout<KS>;
   // Pages are scored in pairs, so a pair's two ring slots are in use while
-  // the next two pages load: kStages - 2 pages ahead.
-  constexpr int kAhead = kStages - 2;
+  // the next two pages load: kAnyStages - 2 pages ahead.
+  constexpr int kAhead = kAnyStages - 2;
   static_assert(kAhead >= 1, "ring too short");
   const int B = a.batch;
   const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
@@ -253,7 +257,7 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
     if (issued < count) {
       const bool ok = page_ok(a, pid_next);
       const uint8_t* page = a.kv + (long long)(ok ? pid_next : 0) * a.page_stride;
-      L::issue(ring + ((unsigned)issued % kStages) * L::kStageBytes, page, dma_lanes, wave, lane);
+      L::issue(ring + ((unsigned)issued % kAnyStages) * L::kStageBytes, page, dma_lanes, wave, lane);
       valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
       ++issued;
       if (issued < count) {
@@ -286,8 +290,8 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
       issue_next();
       issue_next();
       wait_page<L::kLoadsPerWave, kAhead>(issued - (n + 1) - 1);  // pages n and n+1
-      const uint8_t* const st[2] = {ring + ((unsigned)n % kStages) * L::kStageBytes,
-                                    ring + ((unsigned)(n + 1) % kStages) * L::kStageBytes};
+      const uint8_t* const st[2] = {ring + ((unsigned)n % kAnyStages) * L::kStageBytes,
+                                    ring + ((unsigned)(n + 1) % kAnyStages) * L::kStageBytes};
       const bool valid[2] = {((valid_bits >> (n & 31)) & 1u) != 0,
                              ((valid_bits >> ((n + 1) & 31)) & 1u) != 0};
       score_pages_any<KS, OUTT, 2>(st, q_lds, w_lds, a, b, j, valid, Hp, wave, lane, partial,
@@ -296,7 +300,7 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
     if (k < pages) {
       issue_next();
       wait_page<L::kLoadsPerWave, kAhead>(issued - n - 1);
-      const uint8_t* const st[1] = {ring + ((unsigned)n % kStages) * L::kStageBytes};
+      const uint8_t* const st[1] = {ring + ((unsigned)n % kAnyStages) * L::kStageBytes};
       const bool valid[1] = {((valid_bits >> (n & 31)) & 1u) != 0};
       score_pages_any<KS, OUTT, 1>(st, q_lds, w_lds, a, b, j, valid, Hp, wave, lane, partial,
                                    lo_ok, hi_ok, hi_any);
@@ -330,7 +334,7 @@ __global__ void __launch_bounds__(256)
   __shared__ int s_pid[kPidTable];
   const int Hp = heads_padded(a.heads);
   uint8_t* ring = smem;
-  uint8_t* q_lds = smem + kStages * PlaneLayout<KS>::kStageBytes;
+  uint8_t* q_lds = smem + kAnyStages * PlaneLayout<KS>::kStageBytes;
   float* w_lds = reinterpret_cast<float*>(q_lds + a.slots * KS * Hp * 128);
   int* s_prefix = reinterpret_cast<int*>(w_lds + a.slots * Hp);
   build_prefix(a.seq_lens, a.batch, a.max_context / kPage, s_prefix, s_wsum);
@@ -376,7 +380,7 @@ const void* mqa_any_kernel_symbol(int ks, int out_dtype) {
 
 size_t mqa_any_lds_bytes(int ks, int hp, int slots) {
   const size_t stage = (size_t)ks * kPlaneBytes + kPage * 4;
-  return kStages * stage + (size_t)slots * ks * hp * 128 + (size_t)slots * hp * 4;
+  return kAnyStages * stage + (size_t)slots * ks * hp * 128 + (size_t)slots * hp * 4;
 }
 
 hipError_t launch_mqa_any(const MqaArgs& a, int ks, int out_dtype, int grid, size_t lds_bytes,
