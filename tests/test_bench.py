@@ -81,3 +81,14 @@ def test_committed_traffic_summaries_name_their_sources():
     for n in names:
         text = open(os.path.join(prof, n)).read()
         assert "kernel_source_sha256:" in text and "traffic_bytes_per_launch:" in text, n
+
+
+def test_every_bench_workload_is_a_named_synthetic_config():
+    import synth
+    for name in bench.WORKLOADS:
+        assert name in synth.SEEDS, name
+    # the small ones build here; the rest share their code paths
+    inp = synth.make_config("tiny_fp8")
+    assert inp.batch == 2 and inp.next_n == 1
+    ix = synth.make_config("indexer_bf16")
+    assert ix.rows == 24
