@@ -421,12 +421,22 @@ def main():
     # average over its launches (equal-size launches)
     achieved = positions * lbpp / (kern_avg * 1e-3) / 1e9
     value = positions * K / (total_ms * 1e-3)
-    # secondary roofline: the method's 2*H*D*next_n flops per KV position on
-    # the matrix cores, against the dense peak of the products' type
-    general = (inp.num_heads, inp.head_dim) != (64, 128)
-    mfma_type = "f16" if general else ("fp8" if inp.variant == "fp8" else "fp4")
+    # matrix-core roofline: the method's 2*H*D*next_n flops per KV position,
+    # against the dense peak of the products' type (FP8 multiplies exactly
+    # widened f16 operands, MXFP4 its e2m1 operands)
+    mfma_type = "f16" if inp.variant == "fp8" else "fp4"
     flops = positions * 2.0 * inp.num_heads * inp.head_dim * inp.next_n
     mfma_tflops = flops / (kern_avg * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[mfma_type]
+    # the bound is the roofline with the longer ideal time per call
+    hbm_s = positions * lbpp / (HBM_PEAK_GBS * 1e9)
+    mfma_s = flops / (peak * 1e12)
+    traffic_gbs = None if traffic is None else traffic * len(slots) / (kern_avg * 1e-3) / 1e9
+    hbm_line = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_gbs}
+    mfma_line = {"bound": "mfma", "achieved": mfma_tflops, "peak": peak, "unit": "TFLOP/s",
+                 "frac": mfma_tflops / peak, "traffic": traffic_gbs,
+                 "traffic_unit": "GB/s of HBM counter bytes"}
 
     line = {
         "metric": METRIC_FMT % (inp.variant, inp.num_heads, inp.head_dim),
@@ -439,7 +449,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if inp.variant == "fp8" else "fp4",
+        "dtype": "f16" if inp.variant == "fp8" else "fp4",
         "data": "synthetic",
         "gb_per_s": alg_bytes * K / (total_ms * 1e-3) / 1e9,
         "config": {
@@ -449,8 +459,8 @@ def main():
             "head_dim": inp.head_dim, "max_context": inp.max_context,
             "kv_positions": positions, "pages": int(inp.num_pages),
             "schedule": args.mode, "kv_replicas": R, "units": U,
-            "products": ("fp8 MFMA" if (inp.num_heads, inp.head_dim) == (64, 128) else
-                         "f16 MFMA of exactly widened e4m3"),
+            "products": ("f16 MFMA of exactly widened e4m3, fp32 sums" if inp.variant == "fp8"
+                         else "scaled e2m1 MFMA, fp32 sums"),
             "timing": ("graph of the %d steps, events around one replay" % K if args.graph else
                        "host launches of prepared calls, " +
                        ("events around every launch" if args.launch_events else
@@ -461,16 +471,11 @@ def main():
             "launch_bytes_per_position": lbpp,
             "algorithmic_bytes_per_launch": positions * lbpp / len(slots),
             "counter_bytes_per_launch": traffic,
-            "mfma": {"achieved": mfma_tflops, "peak": MFMA_PEAK_TFLOPS[mfma_type],
-                     "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_PEAK_TFLOPS[mfma_type],
-                     "products": mfma_type, "flops_per_call": flops},
+            "mfma": dict(mfma_line, products=mfma_type, flops_per_call=flops,
+                         ideal_us=mfma_s * 1e6),
+            "hbm": dict(hbm_line, ideal_us=hbm_s * 1e6),
         },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": (None if traffic is None else
-                        traffic * len(slots) / (kern_avg * 1e-3) / 1e9),
-        },
+        "roofline": mfma_line if mfma_s > hbm_s else hbm_line,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)

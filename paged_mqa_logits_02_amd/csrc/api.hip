@@ -170,10 +170,10 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t prefix = (size_t)(batch + 1) * sizeof(int);
   if (heads == 64 && head_dim == 128) {
-    const size_t lds = mqa_ring_bytes(variant) + prefix;
     for (int s0 = 0; s0 < next_n; s0 += kFastSlots) {
       a.slot0 = s0;
       a.slots = next_n - s0 < kFastSlots ? next_n - s0 : kFastSlots;
+      const size_t lds = mqa_ring_bytes(variant, a.slots) + prefix;
       a.split_skew = split_skew_for(a.slots, variant);
       const int grid = d->cus * blocks_per_cu(*d, a.slots, variant, out_dtype, lds);
       if (launch_mqa(a, a.slots, variant, out_dtype, grid, lds, s) != hipSuccess)
@@ -387,8 +387,9 @@ int32_t mqa_logits_num_units(int device, int32_t next_n, int32_t variant) {
   // one unit per resident workgroup of the first pass of a 64-head, head_dim
   // 128 call: a workgroup pays the start-up of a range (page ids, first page
   // loads, query) once per unit
-  const size_t lds = mqa_ring_bytes(variant) + sizeof(int);
-  return d.cus * blocks_per_cu(d, next_n < kFastSlots ? next_n : kFastSlots, variant, out, lds);
+  const int slots = next_n < kFastSlots ? next_n : kFastSlots;
+  const size_t lds = mqa_ring_bytes(variant, slots) + sizeof(int);
+  return d.cus * blocks_per_cu(d, slots, variant, out, lds);
 }
 
 int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, int32_t variant,

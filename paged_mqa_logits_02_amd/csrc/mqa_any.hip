@@ -7,14 +7,9 @@
 // takes parametric shapes and the FP4 form exactly 64 heads of 128.)
 //
 // Products: the e4m3 operands are widened exactly to f16 in registers and
-// multiplied with the f16 16x16x32 MFMA, which sums at fp32 precision.  The
-// FP8 MFMA forms keep each product only down to 2^-13 of the largest product
-// of the instruction (measured on gfx950); with many heads that loss is
-// diluted in the head sum, but with few heads and a short head_dim a cell
-// whose dot product cancels can be off by far more than fp32 accumulation
-// would allow.  The widening costs no throughput here: with the query slice
-// read from LDS, an FP8 product tile would wait on LDS bandwidth for as long
-// as the four f16 tiles take.
+// multiplied with the f16 16x16x32 MFMA, which sums at fp32 precision (the
+// FP8 forms truncate each run of 8 products below 2^-13 of the run's largest,
+// so a cancelling dot product can lose its whole value; see device.hpp).
 //
 // The query slice of a request is kept in LDS rather than in registers, so
 // the head count H and head_dim D are runtime values:
@@ -37,10 +32,7 @@
 namespace pmqa {
 
 constexpr int kPlaneBytes = kPage * 128;  // a 128-byte plane of a page's 64 key rows
-#ifndef PMQA_ANY_STAGES
-#define PMQA_ANY_STAGES kStages
-#endif
-constexpr int kAnyStages = PMQA_ANY_STAGES;  // page ring slots of this kernel
+constexpr int kAnyStages = kStages;  // page ring slots of this kernel
 
 __host__ __device__ constexpr int heads_padded(int h) { return (h + 31) / 32 * 32; }
 
@@ -345,9 +337,9 @@ __global__ void __launch_bounds__(256)
   const int32_t* sc = a.schedule;
   bool use_sched = false;
   if (sc != nullptr) {
-    const int h0 = sc[0], h1 = sc[1], h2 = sc[2], h3 = sc[3], h4 = sc[4], h5 = sc[5];
+    const int h0 = sc[0], h1 = sc[1], h2 = sc[2], h3 = sc[3], h4 = sc[4], h5 = sc[5], h6 = sc[6];
     use_sched = (h0 == kSchedMagic) & (h2 == a.next_n) & (h3 == 0) & (h4 == a.max_context) &
-                (h5 == a.batch) & (h1 > 0);
+                (h5 == a.batch) & (h6 == s_prefix[a.batch]) & (h1 > 0);
   }
   if (use_sched) {
     const int U = sc[1];

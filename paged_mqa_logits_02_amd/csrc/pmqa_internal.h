@@ -66,7 +66,8 @@ constexpr int kFastSlots = 4;
 // launches are long enough for the rounds to drift apart, gain ~4%).
 inline int split_skew_for(int slots, int variant) { return slots == 4 && variant == 0 ? 300 : 0; }
 const void* mqa_kernel_symbol(int slots, int variant, int out_dtype);
-size_t mqa_ring_bytes(int variant);  // LDS of the page ring (before the request prefix)
+// LDS before the request prefix of a launch of `slots` query slots
+size_t mqa_ring_bytes(int variant, int slots);
 
 // FP8 kernels for any head count and head_dim: ks = head_dim planes of 128 B
 // (1 or 2).  LDS: ring, query slice, weights, then the request prefix.

@@ -6,13 +6,11 @@
 #include "device.hpp"
 #include "pmqa_internal.h"
 
-#ifndef PMQA_STAGES
-#define PMQA_STAGES 4
-#endif
-
 namespace pmqa {
 
-constexpr int kStages = PMQA_STAGES;
+// LDS ring slots for pages (measured: 5 and 6 slots within noise on the long
+// workloads, fewer resident workgroups for the general kernel's wide shapes).
+constexpr int kStages = 4;
 
 // --------------------------------------------------------------- schedule
 
@@ -213,8 +211,12 @@ template <> struct Frag<0> {
   }
 };
 
-__device__ __forceinline__ v4f mma(const Frag<0>& q, const Frag<0>& k) {
-  return mfma_fp8(q.v, k.v, (v4f){0.f, 0.f, 0.f, 0.f});
+// FP8 operands are multiplied in f16 (exact products, fp32-precision sums): a
+// key fragment is widened once and used by every head tile; a query fragment
+// is widened once per request.
+__device__ __forceinline__ Half32 key_operand(const Frag<0>& k) { return widen32(k.v); }
+__device__ __forceinline__ v4f mma(const Half32& q, const Half32& k) {
+  return mfma_half32(q, k, (v4f){0.f, 0.f, 0.f, 0.f});
 }
 
 // Marks x as redefined here: the empty asm reads and rewrites it, so no use
@@ -272,10 +274,7 @@ __device__ __forceinline__ void wait_page(int ahead) {
   }
 }
 
-#ifndef PMQA_PID_TABLE
-#define PMQA_PID_TABLE 512
-#endif
-constexpr int kPidTable = PMQA_PID_TABLE;  // page ids of the next items, in LDS
+constexpr int kPidTable = 512;  // page ids of the next items, in LDS
 
 // Fills s_pid[0 .. kPidTable) with the page ids of flat items f .. f+kPidTable-1 (up
 // to f_end); entries past the end are not written.  (b, j) is item f's

@@ -228,3 +228,100 @@ def np_nvfp4(packed, scales):
 
 def extent(L, max_context):
     return 0 if L <= 0 else min((L + 63) // 64 * 64, max_context)
+
+
+# ------------------------------------------------ cancelling dot products
+
+
+def pack_e2m1(v):
+    """Values on the e2m1 grid -> packed u8 [..., D/2], even element in the low
+    nibble (exact; asserts that every value is on the grid)."""
+    mag = np.abs(v)
+    idx = np.searchsorted(E2M1_TABLE, mag)
+    assert np.all(E2M1_TABLE[np.minimum(idx, 7)] == mag), "value not on the e2m1 grid"
+    nib = (idx | np.where(v < 0, 8, 0)).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def cancelling_mqa_inputs(variant, next_n, seed, *, one_hot=True, out_dtype="f32", pow2=False):
+    """Inputs whose logits rest on a cancelling dot product.
+
+    Every query slot has one dominant head h* (one-hot weights, or weights
+    2^10 above the rest).  FP8: h*'s q and every key carry a pair q = (256,
+    256), k = (256, -256) in one aligned block of 8 head_dim values, whose
+    products (+-2^16) cancel, plus a tail of positive products in [2^-18,
+    2^-14] of the pair's (values in [0.5, 2]) over the rest of that block and
+    24 other positions; the tail is the whole dot product.  MXFP4: the pair
+    is (6, 6) x (6, -6) in block 0 with small products beside it, and the
+    tail sits in block 2 of h*, whose e8m0 scale is 2^-14 (the other blocks'
+    is 1).  The other heads and key values are small random values.  With
+    pow2 (one-hot only) weights and s_p are powers of two, so the exact
+    result is representable and the sum of the tail is exact in fp32."""
+    rng = np.random.default_rng(seed)
+    inp = synth.make_mqa_inputs([300, 64, 1, 129, 700], next_n, variant=variant, max_context=768,
+                                bt_width=12, seed=seed, out_dtype=out_dtype)
+    B, N, H, D, P = inp.batch, next_n, 64, 128, inp.num_pages
+    w = np.zeros((B * N, H), np.float32)
+    if variant == "fp8":
+        small = lambda shape: np.where(rng.random(shape) < 0.5, -1.0, 1.0) * rng.uniform(  # noqa
+            0.5, 2.0, shape)
+        blk = int(rng.integers(0, 16))
+        d1, d2 = 8 * blk + int(rng.integers(0, 4)), 8 * blk + 4 + int(rng.integers(0, 4))
+        in_blk = [d for d in range(8 * blk, 8 * blk + 8) if d not in (d1, d2)]
+        others = [d for d in range(D) if d // 8 != blk]
+        tail = np.array(in_blk + rng.choice(others, 24, replace=False).tolist())
+        kf = small((P, 64, D))
+        kf[:, :, d1], kf[:, :, d2] = 256.0, -256.0
+        kf[:, :, tail] = rng.uniform(0.5, 2.0, (P, 64, tail.size))
+        qf = small((B, N, H, D))
+        for r in range(B * N):
+            b, t = divmod(r, N)
+            h = int(rng.integers(0, H))
+            qf[b, t, h] = 0.0
+            qf[b, t, h, d1] = qf[b, t, h, d2] = 256.0
+            qf[b, t, h, tail] = rng.uniform(0.5, 2.0, tail.size)
+            sign = 1.0 if rng.random() < 0.75 else -1.0
+            if one_hot:
+                w[r, h] = sign * (2.0 ** int(rng.integers(-2, 3)) if pow2 else rng.uniform(0.5, 2.0))
+            else:
+                w[r] = rng.standard_normal(H) * 2.0 ** -10
+                w[r, h] = sign * rng.uniform(0.5, 2.0)
+        inp.q = synth.encode_e4m3(qf.astype(np.float32))
+        inp.kv[:, : 64 * D] = synth.encode_e4m3(kf.astype(np.float32)).reshape(P, -1)
+        if pow2:
+            sp = np.ldexp(1.0, rng.integers(-3, 4, (P, 64))).astype(np.float32)
+        else:
+            sp = rng.uniform(0.25, 4.0, (P, 64)).astype(np.float32)
+        inp.kv[:, 64 * D: 64 * D + 256] = sp.view(np.uint8)
+    else:
+        grid = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        small = lambda shape: np.where(rng.random(shape) < 0.5, -1.0, 1.0) * rng.choice(  # noqa
+            grid[:3], shape)
+        kf = small((P, 64, D))
+        kf[:, :, 0:32] = 0.0
+        kf[:, :, 0], kf[:, :, 1] = 6.0, -6.0
+        kf[:, :, 2:4] = 0.5
+        kf[:, :, 64:96] = rng.choice(grid, (P, 64, 32))
+        qf = small((B, N, H, D))
+        q_sf = np.full((B, N, H, 4), 127, np.uint8)
+        for r in range(B * N):
+            b, t = divmod(r, N)
+            h = int(rng.integers(0, H))
+            qf[b, t, h] = 0.0
+            qf[b, t, h, 0] = qf[b, t, h, 1] = 6.0
+            qf[b, t, h, 2:4] = 0.5
+            qf[b, t, h, 64:96] = rng.choice(grid, 32)
+            q_sf[b, t, h, 2] = 127 - 14
+            sign = 1.0 if rng.random() < 0.75 else -1.0
+            if one_hot:
+                w[r, h] = sign * 1024.0
+            else:
+                w[r] = rng.standard_normal(H)
+                w[r, h] = sign * 1024.0 * rng.uniform(0.5, 2.0)
+        pack = pack_e2m1
+        inp.q = pack(qf)
+        inp.q_sf = q_sf
+        inp.kv[:, : 64 * D // 2] = pack(kf).reshape(P, -1)
+        inp.kv[:, 64 * D // 2: 64 * D // 2 + 256] = 127
+    inp.weights[:] = w
+    return inp

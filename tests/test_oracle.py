@@ -217,6 +217,23 @@ def test_written_set_follows_extent_and_skips_empty_requests():
             assert m[r, :E].all() and not m[r, E:].any(), (b, L)
 
 
+@pytest.mark.parametrize("next_n", [1, 4])
+def test_written_set_function_equals_dense_written_mask(next_n):
+    """oracle.mqa_written (the written set every full-size GPU check takes) equals
+    the dense oracle's written mask and the extent rule written out here, on
+    lengths 0, negative, 1, 63, 64, 65 and beyond max_context (clamped)."""
+    lens = [0, -7, 1, 63, 64, 65, 200, 256, 1000, 129]
+    inp = synth.make_mqa_inputs(lens, next_n, max_context=256, bt_width=16, seed=19 + next_n)
+    _, _, dense = oracle.mqa_logits_for(inp)
+    fast = oracle.mqa_written(inp.seq_lens, inp.batch, next_n, inp.max_context)
+    rule = np.zeros((len(lens) * next_n, 256), dtype=bool)
+    for b, L in enumerate(lens):
+        cols = 0 if L <= 0 else min(-(-L // 64) * 64, 256)
+        rule[b * next_n:(b + 1) * next_n, :cols] = True
+    assert np.array_equal(fast, dense)
+    assert np.array_equal(fast, rule)
+
+
 def test_meaningful_rows_equal_single_token_calls():
     """Row b*N+t holds the logits of query slot t; its meaningful columns
     0..L-N+t equal a next_n = 1 call with that slot's query and weights."""
@@ -468,3 +485,49 @@ def test_nvfp4_key_scale_doubling_is_exact():
     ref2, _, w2 = oracle.indexer_scores_for(ix2)
     assert np.array_equal(w, w2)
     assert np.array_equal(ref2[w], 2.0 * ref[w])
+
+
+# ------------------------------------------- the cancelling-input fixture
+
+
+def _fp8_run_truncated_dots(q, k):
+    """q [H, D] x k [T, D] -> [H, T], summed the way gfx950's FP8 matrix
+    instructions were measured to sum: within each aligned run of 8 head_dim
+    values every product is truncated toward zero to a multiple of 2^(E-13),
+    E the exponent of the run's largest product; the runs add exactly."""
+    p = q[:, None, :] * k[None, :, :]
+    runs = p.reshape(p.shape[0], p.shape[1], -1, 8)
+    m = np.max(np.abs(runs), axis=-1, keepdims=True)
+    e = np.floor(np.log2(np.where(m > 0, m, 1.0)))
+    u = np.ldexp(1.0, (e - 13).astype(np.int64))
+    t = np.sign(runs) * np.floor(np.abs(runs) / u) * u
+    return t.sum(axis=(-1, -2))
+
+
+@pytest.mark.parametrize("next_n", [1, 4])
+def test_cancelling_fixture_defeats_fp8_run_truncation(next_n):
+    """The GPU tests' cancelling inputs are meant to fail a kernel that sums
+    with the FP8 matrix instructions.  Assembling the logits from dot
+    products summed in that truncated way violates 2e-3*A on most cells, while
+    the same assembly from exact float64 dot products matches the oracle."""
+    from fixtures_util import cancelling_mqa_inputs
+    inp = cancelling_mqa_inputs("fp8", next_n, 300 + next_n)
+    ref, amag, written = oracle.mqa_logits_for(inp)
+    q = decode_queries(inp)
+    N = next_n
+    bad = total = 0
+    for b, (k, sp) in enumerate(decode_keys(inp)):
+        for t in range(N):
+            r = b * N + t
+            w = inp.weights[r].astype(np.float64)
+            trunc = _fp8_run_truncated_dots(q[b, t], k)
+            exact = q[b, t] @ k.T
+            lt = sp * (w @ np.maximum(trunc, 0.0))
+            le = sp * (w @ np.maximum(exact, 0.0))
+            E = k.shape[0]
+            assert written[r, :E].all()
+            np.testing.assert_allclose(le, ref[r, :E], rtol=1e-12, atol=1e-12)
+            tol = 2e-3 * amag[r, :E] + 1e-5
+            bad += int(np.sum(np.abs(lt - ref[r, :E]) > tol))
+            total += E
+    assert total > 0 and bad > 0.9 * total, (bad, total)
