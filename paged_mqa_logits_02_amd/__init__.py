@@ -94,6 +94,87 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ------------------------------------------------------- argument checks
+#
+# The C ABI takes raw device pointers and cannot see how large the buffers
+# behind them are, so a tensor of the wrong dtype, shape or device would make
+# the kernels read or write outside it.  Every tensor is therefore checked
+# here before the call: type and dtype, then shape and size, then layout,
+# then that it lives on the GPU (all on one device).  A bad argument raises
+# ValueError and nothing is launched.
+
+_BYTE_DTYPES = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+
+
+def _need(t, name, dtypes, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s; expected one of %s" % (
+            name, t.dtype, ", ".join(str(d) for d in dtypes)))
+    if dims is not None and t.dim() not in ((dims,) if isinstance(dims, int) else dims):
+        raise ValueError("%s has %d dimensions; expected %s" % (name, t.dim(), dims))
+    return t
+
+
+def _need_numel(t, name, n):
+    if t.numel() < n:
+        raise ValueError("%s has %d elements; at least %d are read" % (name, t.numel(), n))
+
+
+def _need_contiguous(t, name):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _need_device(tensors):
+    """Every tensor on the same GPU; returns that device."""
+    dev = None
+    for name, t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s is on %s; every tensor must be on the GPU" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, dev))
+    return dev
+
+
+def _need_page_bytes(t, name, min_bytes):
+    """A paged cache: pages along dim 0, each page's bytes contiguous and at
+    least min_bytes long."""
+    if t.dim() < 2:
+        raise ValueError("%s needs a page dimension" % name)
+    per_page = t[0].numel() * t.element_size()
+    if per_page < min_bytes:
+        raise ValueError("%s holds %d bytes per page; a page needs %d" % (name, per_page,
+                                                                           min_bytes))
+    if not t[0].is_contiguous():
+        raise ValueError("%s: page contents must be contiguous" % name)
+
+
+def _need_rows(t, name, rows, cols):
+    """A 2-D tensor whose first `rows` rows of `cols` elements are read or written."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError("%s has shape %s; needs at least [%d, %d]" % (name, tuple(t.shape),
+                                                                       rows, cols))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have contiguous rows" % name)
+
+
+def _check_schedule(schedule_meta):
+    if schedule_meta is None:
+        return
+    _need(schedule_meta, "schedule_meta", _I32, 1)
+    _need_numel(schedule_meta, "schedule_meta", schedule_ints(1))
+    _need_contiguous(schedule_meta, "schedule_meta")
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -164,6 +245,12 @@ def mqa_logits_schedule(seq_lens: torch.Tensor, next_n: int, variant: int = VARI
 
 
 def _schedule_args(seq_lens, next_n, variant, max_context, num_units_, out, stream):
+    _need(seq_lens, "seq_lens", _I32, 1)
+    _need_contiguous(seq_lens, "seq_lens")
+    if out is not None:
+        _need(out, "out", _I32, 1)
+        _need_contiguous(out, "out")
+    _need_device([("seq_lens", seq_lens), ("out", out)])
     if num_units_ == 0:
         num_units_ = num_units(next_n, variant, seq_lens.device.index)
     n = schedule_ints(num_units_)
@@ -202,15 +289,47 @@ def _dtype_code(dtype):
     raise ValueError("unsupported output dtype %s" % dtype)
 
 
+def _check_mqa(q, q_sf, kv_fused, weights, seq_lens, block_table, out, schedule_meta,
+               page_min_bytes, q_row_bytes):
+    """Checks shared by both variants; q [B, N, H, q_row_bytes] bytes."""
+    B, N, H = q.shape[:3]
+    _need_contiguous(q, "q")
+    if q.shape[3] * q.element_size() != q_row_bytes:
+        raise ValueError("q rows hold %d bytes; expected %d" % (q.shape[3] * q.element_size(),
+                                                               q_row_bytes))
+    _need(kv_fused, "kv_fused", _BYTE_DTYPES)
+    _need_page_bytes(kv_fused, "kv_fused", page_min_bytes)
+    _need(weights, "weights", (torch.float32,))
+    _need_numel(weights, "weights", B * N * H)
+    _need_contiguous(weights, "weights")
+    _need(seq_lens, "seq_lens", _I32, 1)
+    _need_numel(seq_lens, "seq_lens", B)
+    _need_contiguous(seq_lens, "seq_lens")
+    _need(block_table, "block_table", _I32, 2)
+    if block_table.shape[0] < B:
+        raise ValueError("block_table has %d rows; batch is %d" % (block_table.shape[0], B))
+    if out is not None:
+        _need(out, "out", (torch.float32, torch.bfloat16), 2)
+    _check_schedule(schedule_meta)
+    return _need_device([("q", q), ("q_sf", q_sf), ("kv_fused", kv_fused),
+                         ("weights", weights), ("seq_lens", seq_lens),
+                         ("block_table", block_table), ("out", out),
+                         ("schedule_meta", schedule_meta)])
+
+
 def _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
               schedule_meta, output_dtype, acc_dtype, stream):
+    _need(q, "q", _BYTE_DTYPES, 4)
     B, N, H, D = q.shape
     if next_n is not None and next_n != N:
         raise ValueError("next_n does not match q")
+    _check_mqa(q, None, kv_fused, weights, seq_lens, block_table, out, schedule_meta,
+               PAGE * (D + 4), D)
     bt_stride, bt_width = _rows_of(block_table)
     if max_context is None:
         max_context = out.shape[1] if out is not None else bt_width * PAGE
     out = _out_for(out, B * N, max_context, output_dtype, q.device)
+    _need_rows(out, "out", B * N, max_context)
     ors, _ = _rows_of(out)
     ps, npages = _pages(kv_fused)
     acc = _dtype_code(acc_dtype) if acc_dtype in (torch.float32, torch.bfloat16) else 99
@@ -239,13 +358,22 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
 
 def _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n, sf_vec_size,
                 is_kv_sf_interleaved, max_context, out, schedule_meta, output_dtype, stream):
+    _need(q, "q", (torch.uint8, torch.int8), 4)
     B, N, H, Dh = q.shape
     if next_n is not None and next_n != N:
         raise ValueError("next_n does not match q")
+    _need(q_sf, "q_sf", (torch.uint8, torch.int8, torch.float8_e8m0fnu), 4)
+    if tuple(q_sf.shape[:3]) != (B, N, H) or q_sf.shape[3] * max(sf_vec_size, 1) != 2 * Dh:
+        raise ValueError("q_sf has shape %s; expected [%d, %d, %d, %d]" % (
+            tuple(q_sf.shape), B, N, H, 2 * Dh // max(sf_vec_size, 1)))
+    _need_contiguous(q_sf, "q_sf")
+    _check_mqa(q, q_sf, kv_fused, weights, seq_lens, block_table, out, schedule_meta,
+               PAGE * (Dh + 2 * Dh // 32), Dh)
     bt_stride, bt_width = _rows_of(block_table)
     if max_context is None:
         max_context = out.shape[1] if out is not None else bt_width * PAGE
     out = _out_for(out, B * N, max_context, output_dtype, q.device)
+    _need_rows(out, "out", B * N, max_context)
     ors, _ = _rows_of(out)
     ps, npages = _pages(kv_fused)
     return out, (_ptr(q), _ptr(q_sf), sf_vec_size, int(is_kv_sf_interleaved), _ptr(kv_fused), ps,
@@ -328,8 +456,50 @@ def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, 
     return scores
 
 
+def _check_indexer(query, key_cache, block_table, context_lengths, requests, scores,
+                   query_scales, key_scales, group_row_offsets):
+    nvfp4 = query_scales is not None or key_scales is not None
+    if nvfp4:
+        _need(query, "query", (torch.uint8, torch.int8), 2)
+        if query_scales is None or key_scales is None:
+            raise ValueError("NVFP4 inputs need both query_scales and key_scales")
+        _need(query_scales, "query_scales", _BYTE_DTYPES)
+        rows = query.shape[0]
+        _need_numel(query_scales, "query_scales", rows * query.shape[1] // 8)
+        _need_contiguous(query_scales, "query_scales")
+        _need(key_cache, "key_cache", _BYTE_DTYPES)
+        _need_page_bytes(key_cache, "key_cache", PAGE * query.shape[1])
+        _need(key_scales, "key_scales", _BYTE_DTYPES)
+        _need_page_bytes(key_scales, "key_scales", PAGE * query.shape[1] // 8)
+    else:
+        _need(query, "query", (torch.bfloat16,), 2)
+        rows = query.shape[0]
+        _need(key_cache, "key_cache", (torch.bfloat16,) + _BYTE_DTYPES)
+        _need_page_bytes(key_cache, "key_cache", PAGE * query.shape[1] * 2)
+    _need_contiguous(query, "query")
+    _need(block_table, "block_table", _I32, 2)
+    _need(context_lengths, "context_lengths", _I32, 1)
+    _need_contiguous(context_lengths, "context_lengths")
+    groups = context_lengths.shape[0]
+    _need(requests, "requests", _I32, 1)
+    _need_numel(requests, "requests", groups)
+    _need_contiguous(requests, "requests")
+    if group_row_offsets is not None:
+        _need(group_row_offsets, "group_row_offsets", _I32, 1)
+        _need_numel(group_row_offsets, "group_row_offsets", groups + 1)
+        _need_contiguous(group_row_offsets, "group_row_offsets")
+    _need(scores, "scores", (torch.float32,), 2)
+    _need_rows(scores, "scores", rows, scores.shape[1])
+    _need_device([("query", query), ("key_cache", key_cache), ("block_table", block_table),
+                  ("context_lengths", context_lengths), ("requests", requests),
+                  ("scores", scores), ("query_scales", query_scales),
+                  ("key_scales", key_scales), ("group_row_offsets", group_row_offsets)])
+
+
 def _indexer_args(query, key_cache, block_table, context_lengths, requests, scores,
                   query_scales, key_scales, group_row_offsets, stream):
+    _check_indexer(query, key_cache, block_table, context_lengths, requests, scores,
+                   query_scales, key_scales, group_row_offsets)
     bt_stride, bt_width = _rows_of(block_table)
     srs, max_context = _rows_of(scores)
     ps, npages = _pages(key_cache)
