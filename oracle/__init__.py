@@ -55,10 +55,11 @@ def _load():
             lib = ctypes.CDLL(_LIB)
             P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
             lib.oracle_mqa_logits.argtypes = [ctypes.c_int, P, P, P, I64, P, P, P, I64,
-                                              I32, I32, I32, I32, I32, P, P, P, ctypes.c_int]
+                                              I32, I32, I32, I32, I32, I32, I32, P, P, P,
+                                              ctypes.c_int]
             lib.oracle_mqa_logits_points.argtypes = [ctypes.c_int, P, P, P, I64, P, P, P, I64,
-                                                     I32, I32, I32, I32, I32, I64, P, P,
-                                                     P, P, P, ctypes.c_int]
+                                                     I32, I32, I32, I32, I32, I32, I32, I64, P,
+                                                     P, P, P, P, ctypes.c_int]
             lib.oracle_mqa_written.argtypes = [P, I32, I32, I32, P]
             lib.oracle_indexer_scores.argtypes = [P, I32, I32, P, I64, P, I64, P, P, P, I32, I32,
                                                   P, P, P, ctypes.c_int]
@@ -109,12 +110,14 @@ def _c(a, dtype):
 
 
 def mqa_logits(variant, q, q_sf, kv, page_stride, weights, seq_lens, block_table,
-               batch, next_n, num_heads, head_dim, max_context, nthreads=None):
+               batch, next_n, num_heads, head_dim, max_context, nthreads=None, *,
+               sf_vec_size=32, kv_sf_interleaved=False):
     """Dense oracle.  Returns (ref, amag, written), each [batch*next_n, max_context].
 
     ref     float64 logits where written, NaN elsewhere
     amag    s_p * sum_h |w| * relu(q.k), the magnitude the tolerance scales with
     written bool, the cells the operation writes
+    sf_vec_size / kv_sf_interleaved: the MXFP4 scale layout (see oracle.c)
     """
     lib = _load()
     rows = batch * next_n
@@ -126,6 +129,7 @@ def mqa_logits(variant, q, q_sf, kv, page_stride, weights, seq_lens, block_table
     rc = lib.oracle_mqa_logits(0 if variant == "fp8" else 1, _ptr(q), _ptr(q_sf), _ptr(kv),
                                int(page_stride), _ptr(w), _ptr(sl), _ptr(bt), int(bt.shape[1]),
                                batch, next_n, num_heads, head_dim, max_context,
+                               int(sf_vec_size), int(bool(kv_sf_interleaved)),
                                _ptr(ref), _ptr(amag), _ptr(written),
                                nthreads or default_threads())
     if rc != 0:
@@ -135,7 +139,7 @@ def mqa_logits(variant, q, q_sf, kv, page_stride, weights, seq_lens, block_table
 
 def mqa_logits_points(variant, q, q_sf, kv, page_stride, weights, seq_lens, block_table,
                       batch, next_n, num_heads, head_dim, max_context, rows, cols,
-                      nthreads=None):
+                      nthreads=None, *, sf_vec_size=32, kv_sf_interleaved=False):
     """Oracle at the given (row, column) cells.  Returns (ref, amag, written)."""
     lib = _load()
     rows = np.ascontiguousarray(rows, dtype=np.int32)
@@ -148,7 +152,9 @@ def mqa_logits_points(variant, q, q_sf, kv, page_stride, weights, seq_lens, bloc
     rc = lib.oracle_mqa_logits_points(0 if variant == "fp8" else 1, _ptr(q), _ptr(q_sf),
                                       _ptr(kv), int(page_stride), _ptr(w), _ptr(sl), _ptr(bt),
                                       int(bt.shape[1]), batch, next_n, num_heads, head_dim,
-                                      max_context, n, _ptr(rows), _ptr(cols), _ptr(ref),
+                                      max_context, int(sf_vec_size),
+                                      int(bool(kv_sf_interleaved)), n, _ptr(rows), _ptr(cols),
+                                      _ptr(ref),
                                       _ptr(amag), _ptr(written), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_mqa_logits_points: bad arguments (%d)" % rc)
@@ -159,14 +165,18 @@ def mqa_logits_for(inp, nthreads=None):
     """Dense oracle for a ``synth.MqaInputs``."""
     return mqa_logits(inp.variant, inp.q, inp.q_sf, inp.kv, inp.page_stride, inp.weights,
                       inp.seq_lens, inp.block_table, inp.batch, inp.next_n, inp.num_heads,
-                      inp.head_dim, inp.max_context, nthreads)
+                      inp.head_dim, inp.max_context, nthreads,
+                      sf_vec_size=getattr(inp, "sf_vec_size", 32),
+                      kv_sf_interleaved=getattr(inp, "kv_sf_interleaved", False))
 
 
 def mqa_logits_points_for(inp, rows, cols, nthreads=None):
     return mqa_logits_points(inp.variant, inp.q, inp.q_sf, inp.kv, inp.page_stride,
                              inp.weights, inp.seq_lens, inp.block_table, inp.batch,
                              inp.next_n, inp.num_heads, inp.head_dim, inp.max_context,
-                             rows, cols, nthreads)
+                             rows, cols, nthreads,
+                             sf_vec_size=getattr(inp, "sf_vec_size", 32),
+                             kv_sf_interleaved=getattr(inp, "kv_sf_interleaved", False))
 
 
 def mqa_written(seq_lens, batch, next_n, max_context):

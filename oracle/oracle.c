@@ -32,6 +32,12 @@
  *     FP4 byte is its low nibble;
  *   - FP8 page layout: 64 tokens x D bytes, then 64 little-endian fp32 scales;
  *     MXFP4 page layout: 64 tokens x D/2 bytes, then 64 x D/32 e8m0 codes;
+ *   - MXFP4 with sf_vec_size = 16 (the attn_scores paragraph names
+ *     sf_vec_size and is_kv_sf_interleaved without defining them): one e8m0
+ *     code per 16 values instead of 32, for q_sf [B, N, H, D/16] and for the
+ *     keys (D/16 codes per token); with is_kv_sf_interleaved = 1 a page holds
+ *     64 token records, each the token's D/2 packed bytes followed by its
+ *     D/sf_vec_size codes (same page size as the trailing layout);
  *   - the block table is int32 [B, bt_stride], page j of request b is
  *     block_table[b*bt_stride + j]; page i starts at kv + i*page_stride.
  *
@@ -133,6 +139,8 @@ typedef struct {
     const int32_t* bt;
     int64_t bt_stride;
     int32_t B, N, H, D, max_context;
+    int32_t sfv;         /* MXFP4: values per e8m0 code (32 or 16) */
+    int32_t interleaved; /* MXFP4: 1 = each token's codes follow its packed bytes */
 } mqa_args;
 
 /* Decoded key vector of KV position p of request b (float64), and its s_p. */
@@ -148,12 +156,20 @@ static double decode_key(const mqa_args* a, int32_t b, int64_t p, double* k)
             k[d] = oracle_e4m3(row[d]);
         return f32_at(pg + (int64_t)TOK_PER_PAGE * D + j * 4); /* s_p */
     } else {
-        const uint8_t* row = pg + j * (D / 2);
-        const uint8_t* sf = pg + (int64_t)TOK_PER_PAGE * (D / 2) + j * (D / 32);
+        int nsf = D / a->sfv; /* codes per token */
+        const uint8_t* row;
+        const uint8_t* sf;
+        if (a->interleaved) {
+            row = pg + j * (D / 2 + nsf);
+            sf = row + D / 2;
+        } else {
+            row = pg + j * (D / 2);
+            sf = pg + (int64_t)TOK_PER_PAGE * (D / 2) + j * nsf;
+        }
         for (d = 0; d < D; ++d) {
             uint8_t byte = row[d / 2];
             uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
-            k[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / 32]);
+            k[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / a->sfv]);
         }
         return 1.0; /* MXFP4 has no per-position factor */
     }
@@ -170,11 +186,11 @@ static void decode_query(const mqa_args* a, int32_t b, int32_t t, int32_t h, dou
             qv[d] = oracle_e4m3(row[d]);
     } else {
         const uint8_t* row = a->q + qi * (D / 2);
-        const uint8_t* sf = a->q_sf + qi * (D / 32);
+        const uint8_t* sf = a->q_sf + qi * (D / a->sfv);
         for (d = 0; d < D; ++d) {
             uint8_t byte = row[d / 2];
             uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
-            qv[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / 32]);
+            qv[d] = oracle_e2m1(nib) * oracle_e8m0(sf[d / a->sfv]);
         }
     }
 }
@@ -276,19 +292,22 @@ static int mqa_check(const mqa_args* a)
 {
     if (a->B < 0 || a->N < 1 || a->H < 1 || a->D < 1 || a->max_context < 0)
         return -2;
-    if (a->variant == 1 && a->D % 32 != 0)
+    if (a->variant == 1 && ((a->sfv != 32 && a->sfv != 16) || a->D % a->sfv != 0 ||
+                            (a->interleaved != 0 && a->interleaved != 1)))
         return -2;
     return 0;
 }
 
+/* sfv / interleaved describe the MXFP4 scale layout (32 / 0 is the layout of
+ * the variant's defaults); they are ignored for FP8. */
 int oracle_mqa_logits(int variant, const uint8_t* q, const uint8_t* q_sf, const uint8_t* kv,
                       int64_t page_stride, const float* w, const int32_t* seq_lens,
                       const int32_t* bt, int64_t bt_stride, int32_t B, int32_t N, int32_t H,
-                      int32_t D, int32_t max_context, double* ref, double* amag,
-                      uint8_t* written, int nthreads)
+                      int32_t D, int32_t max_context, int32_t sfv, int32_t interleaved,
+                      double* ref, double* amag, uint8_t* written, int nthreads)
 {
     mqa_args a = {variant, q, q_sf, kv, page_stride, w, seq_lens, bt, bt_stride,
-                  B, N, H, D, max_context};
+                  B, N, H, D, max_context, sfv, interleaved};
     int rc = mqa_check(&a);
     if (rc)
         return rc;
@@ -299,11 +318,12 @@ int oracle_mqa_logits_points(int variant, const uint8_t* q, const uint8_t* q_sf,
                              const uint8_t* kv, int64_t page_stride, const float* w,
                              const int32_t* seq_lens, const int32_t* bt, int64_t bt_stride,
                              int32_t B, int32_t N, int32_t H, int32_t D, int32_t max_context,
-                             int64_t npts, const int32_t* rows, const int32_t* cols,
-                             double* ref, double* amag, uint8_t* written, int nthreads)
+                             int32_t sfv, int32_t interleaved, int64_t npts, const int32_t* rows,
+                             const int32_t* cols, double* ref, double* amag, uint8_t* written,
+                             int nthreads)
 {
     mqa_args a = {variant, q, q_sf, kv, page_stride, w, seq_lens, bt, bt_stride,
-                  B, N, H, D, max_context};
+                  B, N, H, D, max_context, sfv, interleaved};
     int rc = mqa_check(&a);
     if (rc)
         return rc;

@@ -83,17 +83,18 @@ _E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
 _E2M1_TIE_UP = np.array([False, True, False, True, False, True, False])
 
 
-def quantize_mxfp4(x: np.ndarray):
-    """OCP MX quantisation with 32-element blocks along the last axis.
+def quantize_mxfp4(x: np.ndarray, block: int = 32):
+    """OCP MX quantisation with `block`-element blocks along the last axis
+    (32 in the OCP format; 16 for the sf_vec_size = 16 layout).
 
     shared exponent = floor(log2(amax)) - 2 (e2m1's largest exponent is 2),
     elements rounded to nearest even on the e2m1 grid and clamped to +-6.
-    Returns (packed uint8 [..., D/2], scale codes uint8 [..., D/32]).
+    Returns (packed uint8 [..., D/2], scale codes uint8 [..., D/block]).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     D = x.shape[-1]
-    assert D % 32 == 0
-    xb = x.reshape(x.shape[:-1] + (D // 32, 32))
+    assert D % block == 0
+    xb = x.reshape(x.shape[:-1] + (D // block, block))
     amax = np.max(np.abs(xb), axis=-1)
     _, e = np.frexp(amax)  # amax = m * 2**e, m in [0.5, 1)
     shared = np.where(amax > 0, e.astype(np.int32) - 1 - 2, 0)
@@ -148,7 +149,7 @@ class MqaInputs:
     head_dim: int
     max_context: int
     q: np.ndarray  # fp8: u8 [B,N,H,D]; mxfp4: u8 [B,N,H,D/2]
-    q_sf: Optional[np.ndarray]  # mxfp4: u8 [B,N,H,D/32]; fp8: None
+    q_sf: Optional[np.ndarray]  # mxfp4: u8 [B,N,H,D/sf_vec_size]; fp8: None
     kv: np.ndarray  # u8 [num_pages, page_stride]
     page_stride: int
     weights: np.ndarray  # f32 [B*N, H]
@@ -156,6 +157,8 @@ class MqaInputs:
     block_table: np.ndarray  # i32 [B, W]
     out_dtype: str  # "f32" or "bf16"
     name: str = ""
+    sf_vec_size: int = 32  # mxfp4: values per e8m0 code
+    kv_sf_interleaved: bool = False  # mxfp4: each token's codes follow its packed bytes
 
     @property
     def num_pages(self) -> int:
@@ -169,14 +172,25 @@ class MqaInputs:
         return int(np.minimum(np.maximum(self.seq_lens, 0), self.max_context).sum())
 
 
-def page_bytes(variant: str, head_dim: int) -> int:
-    """Minimum bytes of one page: 64 tokens of keys, then their scales."""
+def page_bytes(variant: str, head_dim: int, sf_vec_size: int = 32) -> int:
+    """Minimum bytes of one page: 64 tokens of keys and their scales."""
     if variant == "fp8":
         return PAGE * head_dim + PAGE * 4
-    return PAGE * (head_dim // 2) + PAGE * (head_dim // 32)
+    return PAGE * (head_dim // 2) + PAGE * (head_dim // sf_vec_size)
 
 
-def _fill_pages(rng, variant, num_pages, head_dim, page_stride, chunk=2048):
+def mxfp4_page(packed, sf, interleaved):
+    """One MXFP4 page's bytes from packed keys u8 [..., 64, D/2] and codes
+    u8 [..., 64, D/sfv]: all packed rows then all codes, or (interleaved) 64
+    token records of packed bytes followed by that token's codes."""
+    lead = packed.shape[:-2]
+    if interleaved:
+        return np.concatenate([packed, sf], axis=-1).reshape(lead + (-1,))
+    return np.concatenate([packed.reshape(lead + (-1,)), sf.reshape(lead + (-1,))], axis=-1)
+
+
+def _fill_pages(rng, variant, num_pages, head_dim, page_stride, chunk=2048, sf_vec_size=32,
+                interleaved=False):
     """Every token slot of every page (tails included) holds valid data."""
     kv = np.zeros((num_pages, page_stride), dtype=np.uint8)
     kbytes = PAGE * head_dim if variant == "fp8" else PAGE * head_dim // 2
@@ -188,16 +202,17 @@ def _fill_pages(rng, variant, num_pages, head_dim, page_stride, chunk=2048):
             kv[p0:p1, :kbytes] = codes.reshape(p1 - p0, -1)
             kv[p0:p1, kbytes:kbytes + PAGE * 4] = s.view(np.uint8).reshape(p1 - p0, -1)
         else:
-            packed, sf = quantize_mxfp4(k)
-            kv[p0:p1, :kbytes] = packed.reshape(p1 - p0, -1)
-            kv[p0:p1, kbytes:kbytes + PAGE * head_dim // 32] = sf.reshape(p1 - p0, -1)
+            packed, sf = quantize_mxfp4(k, sf_vec_size)
+            pg = mxfp4_page(packed, sf, interleaved)
+            kv[p0:p1, :pg.shape[1]] = pg
     return kv
 
 
 def make_mqa_inputs(seq_lens, next_n, *, variant="fp8", num_heads=64, head_dim=128,
                     max_context=None, bt_width=None, w_std=1.0, seed=0,
                     full_table=False, extra_pages=0, page_stride=None,
-                    out_dtype=None, name="") -> MqaInputs:
+                    out_dtype=None, name="", sf_vec_size=32,
+                    kv_sf_interleaved=False) -> MqaInputs:
     """Build one paged MQA logits workload.
 
     Physical page ids are a random permutation; request b owns the next
@@ -218,7 +233,7 @@ def make_mqa_inputs(seq_lens, next_n, *, variant="fp8", num_heads=64, head_dim=1
     num_pages = B * bt_width if full_table else need + extra_pages
     num_pages = max(num_pages, 1)
     if page_stride is None:
-        page_stride = page_bytes(variant, D)
+        page_stride = page_bytes(variant, D, sf_vec_size)
 
     # draws: q, then weights, then page permutation, then page contents
     qf = rng.standard_normal((B, N, H, D), dtype=np.float32)
@@ -226,7 +241,7 @@ def make_mqa_inputs(seq_lens, next_n, *, variant="fp8", num_heads=64, head_dim=1
         q = quantize_fp8_per_tensor(qf)
         q_sf = None
     else:
-        q, q_sf = quantize_mxfp4(qf)
+        q, q_sf = quantize_mxfp4(qf, sf_vec_size)
     weights = (rng.standard_normal((B * N, H), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
     perm = rng.permutation(num_pages).astype(np.int32)
     if full_table:
@@ -238,11 +253,13 @@ def make_mqa_inputs(seq_lens, next_n, *, variant="fp8", num_heads=64, head_dim=1
             T = min(T, bt_width)
             block_table[b, :T] = perm[pos:pos + T]
             pos += T
-    kv = _fill_pages(rng, variant, num_pages, D, page_stride)
+    kv = _fill_pages(rng, variant, num_pages, D, page_stride, sf_vec_size=sf_vec_size,
+                     interleaved=kv_sf_interleaved)
     if out_dtype is None:
         out_dtype = "f32" if variant == "fp8" else "bf16"
     return MqaInputs(variant, B, N, H, D, int(max_context), q, q_sf, kv, int(page_stride),
-                     weights, seq_lens, block_table, out_dtype, name)
+                     weights, seq_lens, block_table, out_dtype, name, int(sf_vec_size),
+                     bool(kv_sf_interleaved))
 
 
 # --------------------------------------------------------------------------

@@ -59,10 +59,23 @@ def e2m1_code(v):
     return idx | (8 if v < 0 else 0)
 
 
+def mx_page_fields(pg, D, sfv, interleaved):
+    """(packed u8 [64, D/2], codes u8 [64, D/sfv]) of one MXFP4 page's bytes:
+    all packed rows then all codes, or 64 records of packed bytes + codes."""
+    nsf = D // sfv
+    if interleaved:
+        rec = pg[: 64 * (D // 2 + nsf)].reshape(64, D // 2 + nsf)
+        return rec[:, : D // 2], rec[:, D // 2:]
+    return pg[: 64 * D // 2].reshape(64, D // 2), pg[64 * D // 2: 64 * D // 2 + 64 * nsf].reshape(
+        64, nsf)
+
+
 def decode_keys(inp):
     """Per request: (k float64 [E_b, D], s float64 [E_b]) over the written extent."""
     out = []
     D = inp.head_dim
+    sfv = getattr(inp, "sf_vec_size", 32)
+    il = getattr(inp, "kv_sf_interleaved", False)
     for b in range(inp.batch):
         L = int(inp.seq_lens[b])
         E = 0 if L <= 0 else min((L + 63) // 64 * 64, inp.max_context)
@@ -73,9 +86,9 @@ def decode_keys(inp):
                 ks.append(np_e4m3(pg[: 64 * D].reshape(64, D)))
                 ss.append(pg[64 * D: 64 * D + 256].view(np.float32).astype(np.float64))
             else:
-                vals = np_e2m1_unpack(pg[: 64 * D // 2].reshape(64, D // 2))
-                sf = np_e8m0(pg[64 * D // 2: 64 * D // 2 + 64 * D // 32].reshape(64, D // 32))
-                ks.append(vals * np.repeat(sf, 32, axis=1))
+                packed, codes = mx_page_fields(pg, D, sfv, il)
+                vals = np_e2m1_unpack(packed)
+                ks.append(vals * np.repeat(np_e8m0(codes), sfv, axis=1))
                 ss.append(np.ones(64))
         out.append((np.concatenate(ks) if ks else np.zeros((0, D)),
                     np.concatenate(ss) if ss else np.zeros(0)))
@@ -88,7 +101,7 @@ def decode_queries(inp):
         return np_e4m3(inp.q)
     vals = np_e2m1_unpack(inp.q)
     sf = np_e8m0(inp.q_sf)
-    return vals * np.repeat(sf, 32, axis=-1)
+    return vals * np.repeat(sf, getattr(inp, "sf_vec_size", 32), axis=-1)
 
 
 def flip_key_signs(inp):
@@ -99,6 +112,10 @@ def flip_key_signs(inp):
     D = inp.head_dim
     if inp.variant == "fp8":
         kv[:, : 64 * D] ^= 0x80
+    elif getattr(inp, "kv_sf_interleaved", False):
+        rec = D // 2 + D // getattr(inp, "sf_vec_size", 32)
+        view = kv[:, : 64 * rec].reshape(kv.shape[0], 64, rec)
+        view[:, :, : D // 2] ^= 0x88
     else:
         kv[:, : 64 * D // 2] ^= 0x88
     out.kv = kv
@@ -137,9 +154,15 @@ def mqa_from_case(case, variant):
             kv[page, 64 * D + 4 * slot: 64 * D + 4 * slot + 4] = np.array(
                 [tk["s"]], dtype=np.float32).view(np.uint8)
     else:
+        sfv = case.get("sf_vec_size", 32)
+        il = bool(case.get("interleaved", False))
+        nsf = D // sfv
+        stride = synth.page_bytes(variant, D, sfv)
+        kv = np.zeros((P, stride), dtype=np.uint8)
         q = np.zeros((1, 1, H, D // 2), dtype=np.uint8)
-        q_sf = np.full((1, 1, H, D // 32), 127, dtype=np.uint8)
-        kv[:, 64 * D // 2: 64 * D // 2 + 64 * D // 32] = 127
+        q_sf = np.full((1, 1, H, nsf), 127, dtype=np.uint8)
+        packed = np.zeros((P, 64, D // 2), dtype=np.uint8)
+        codes = np.full((P, 64, nsf), 127, dtype=np.uint8)
         for hd in case["heads"]:
             w[0, hd["h"]] = hd["w"]
             for d, v in hd["q"].items():
@@ -152,14 +175,21 @@ def mqa_from_case(case, variant):
             page, slot = case["block_table"][p // 64], p % 64
             for d, v in tk["k"].items():
                 d = int(d)
-                kv[page, slot * D // 2 + d // 2] |= e2m1_code(v) << (4 * (d & 1))
+                packed[page, slot, d // 2] |= e2m1_code(v) << (4 * (d & 1))
             for g, c in tk.get("sf", {}).items():
-                kv[page, 64 * D // 2 + slot * D // 32 + int(g)] = c
+                codes[page, slot, int(g)] = c
+        if il:  # 64 records: a token's packed bytes, then its codes
+            kv[:, :] = np.concatenate([packed, codes], axis=2).reshape(P, -1)
+        else:
+            kv[:, :] = np.concatenate([packed.reshape(P, -1), codes.reshape(P, -1)], axis=1)
     L = case["seq_len"]
     max_context = max(64, (L + 63) // 64 * 64)
-    return synth.MqaInputs(variant, 1, 1, H, D, max_context, q, q_sf, kv, stride, w,
-                           np.array([L], dtype=np.int32), bt,
-                           "f32" if variant == "fp8" else "bf16", case["name"])
+    inp = synth.MqaInputs(variant, 1, 1, H, D, max_context, q, q_sf, kv, stride, w,
+                          np.array([L], dtype=np.int32), bt,
+                          "f32" if variant == "fp8" else "bf16", case["name"])
+    if variant != "fp8":
+        inp.sf_vec_size, inp.kv_sf_interleaved = sfv, il
+    return inp
 
 
 def indexer_from_case(case):

@@ -531,3 +531,71 @@ def test_cancelling_fixture_defeats_fp8_run_truncation(next_n):
             bad += int(np.sum(np.abs(lt - ref[r, :E]) > tol))
             total += E
     assert total > 0 and bad > 0.9 * total, (bad, total)
+
+
+# ---------------------------------------------- MXFP4 scale layouts (readings)
+
+MX_LAYOUTS = [(32, False), (16, False), (32, True), (16, True)]
+
+
+@pytest.mark.parametrize("case", load_golden("mxfp4_layout_cases.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_mxfp4_layout_golden(case):
+    inp = mqa_from_case(case, "mxfp4")
+    ref, _, written = oracle.mqa_logits_for(inp)
+    E = extent(case["seq_len"], inp.max_context)
+    assert written[0, :E].all() and not written[0, E:].any()
+    for col, v in case["expected"].items():
+        assert ref[0, int(col)] == v, (case["name"], col)
+
+
+@pytest.mark.parametrize("sfv,il", MX_LAYOUTS)
+def test_mxfp4_layout_rectifier_identities(sfv, il):
+    """The two rectifier identities, against float64 matrix products of values
+    decoded independently (numpy, library e8m0 cast) in each scale layout."""
+    inp = synth.make_mqa_inputs([37, 0, 130, 64], 2, variant="mxfp4", max_context=192,
+                                bt_width=3, seed=13, sf_vec_size=sfv, kv_sf_interleaved=il)
+    r1, a1, m = oracle.mqa_logits_for(inp)
+    r2, _, m2 = oracle.mqa_logits_for(flip_key_signs(inp))
+    assert np.array_equal(m, m2)
+    lin = _weighted_query_dot(inp, "lin")
+    ab = _weighted_query_dot(inp, "abs")
+    np.testing.assert_allclose((r1 - r2)[m], lin[m], rtol=1e-12, atol=1e-9 * np.max(a1))
+    np.testing.assert_allclose((r1 + r2)[m], ab[m], rtol=1e-12, atol=1e-9 * np.max(a1))
+
+
+@pytest.mark.parametrize("sfv", [32, 16])
+def test_mxfp4_interleaved_records_equal_trailing_codes(sfv):
+    """Rearranging every page from the trailing layout (all packed rows, then
+    all codes) into token records (packed row, then that token's codes) --
+    done here with plain slicing -- leaves every logit bit-identical."""
+    inp = synth.make_mqa_inputs([300, 1, 129], 3, variant="mxfp4", max_context=320,
+                                bt_width=5, seed=14, sf_vec_size=sfv)
+    base, _, m = oracle.mqa_logits_for(inp)
+    D, nsf, P = 128, 128 // sfv, inp.num_pages
+    rec = copy.copy(inp)
+    kv = np.zeros_like(inp.kv)
+    for t in range(64):
+        kv[:, t * (D // 2 + nsf): t * (D // 2 + nsf) + D // 2] = inp.kv[:, t * D // 2:(t + 1) * D // 2]
+        kv[:, t * (D // 2 + nsf) + D // 2:(t + 1) * (D // 2 + nsf)] = \
+            inp.kv[:, 64 * D // 2 + t * nsf: 64 * D // 2 + (t + 1) * nsf]
+    rec.kv, rec.kv_sf_interleaved = kv, True
+    got, _, m2 = oracle.mqa_logits_for(rec)
+    assert np.array_equal(m, m2) and np.array_equal(got[m], base[m])
+
+
+def test_mxfp4_sixteen_value_codes_that_pair_up_equal_thirty_two():
+    """With sf_vec_size = 16, giving both halves of every 32-value block the
+    same code must equal the sf_vec_size = 32 layout with that code."""
+    inp = synth.make_mqa_inputs([200, 64], 2, variant="mxfp4", max_context=256, bt_width=4,
+                                seed=15, sf_vec_size=32)
+    base, _, m = oracle.mqa_logits_for(inp)
+    D, P = 128, inp.num_pages
+    s16 = copy.copy(inp)
+    s16.q_sf = np.repeat(inp.q_sf, 2, axis=-1)
+    packed = inp.kv[:, : 64 * D // 2]
+    codes = inp.kv[:, 64 * D // 2: 64 * D // 2 + 64 * 4].reshape(P, 64, 4)
+    s16.kv = np.concatenate([packed, np.repeat(codes, 2, axis=-1).reshape(P, -1)], axis=1)
+    s16.page_stride, s16.sf_vec_size = s16.kv.shape[1], 16
+    got, _, m2 = oracle.mqa_logits_for(s16)
+    assert np.array_equal(m, m2) and np.array_equal(got[m], base[m])
