@@ -52,6 +52,9 @@ WORKLOADS = {
     "verify_fp8_bf16": "B=128, next_n=4, H=64, d=128, page 64, seq_lens uniform 4K..64K, "
                        "bf16 out",
     "mxfp4_n4": "B=64, next_n=4, H=64, d=128, page 64, seq_lens uniform 16K..128K, bf16 out",
+    "mxfp4_sf16": "mxfp4 with one e8m0 code per 16 values (8 per token)",
+    "mxfp4_records": "mxfp4 with each token's codes after its packed bytes (68-byte records)",
+    "mxfp4_sf16_records": "mxfp4 with 8 codes per token in 72-byte token records",
     "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
     "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "
@@ -59,13 +62,13 @@ WORKLOADS = {
 }
 
 
-def algorithmic_bytes_per_position(variant, next_n, out_bytes, head_dim=128):
+def algorithmic_bytes_per_position(variant, next_n, out_bytes, head_dim=128, sf_vec_size=32):
     """Bytes the method must move per KV position (page-tail padding, query,
-    weight and block-table reads excluded): the key, its scale, one output
+    weight and block-table reads excluded): the key, its scale(s), one output
     per query slot."""
     if variant == "fp8":
         return head_dim + 4 + next_n * out_bytes
-    return head_dim // 2 + head_dim // 32 + next_n * out_bytes
+    return head_dim // 2 + head_dim // sf_vec_size + next_n * out_bytes
 
 
 def launch_slots(variant, next_n, num_heads, head_dim):
@@ -79,10 +82,10 @@ def launch_slots(variant, next_n, num_heads, head_dim):
     return [min(per, next_n - s) for s in range(0, next_n, per)]
 
 
-def launch_bytes_per_position(variant, next_n, out_bytes, num_heads, head_dim):
+def launch_bytes_per_position(variant, next_n, out_bytes, num_heads, head_dim, sf_vec_size=32):
     """Algorithmic bytes per KV position summed over the launches of a call:
     every launch reads the key and its scale and writes its own slots."""
-    return sum(algorithmic_bytes_per_position(variant, n, out_bytes, head_dim)
+    return sum(algorithmic_bytes_per_position(variant, n, out_bytes, head_dim, sf_vec_size)
                for n in launch_slots(variant, next_n, num_heads, head_dim))
 
 
@@ -311,6 +314,7 @@ def main():
             for _ in range(2)]
     U = pm.num_units(inp.next_n, variant)
     sched = torch.empty(pm.schedule_ints(U), dtype=torch.int32, device=dev)
+    mx_layout = dict(sf_vec_size=inp.sf_vec_size, is_kv_sf_interleaved=inp.kv_sf_interleaved)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, st, ev0=None, ev1=None):
@@ -326,7 +330,7 @@ def main():
                               out=outs[i % 2], schedule_meta=s, stream=st)
         else:
             pm.mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt, max_context=inp.max_context,
-                                out=outs[i % 2], schedule_meta=s, stream=st)
+                                out=outs[i % 2], schedule_meta=s, stream=st, **mx_layout)
         if ev1 is not None:
             ev1.record(st)
 
@@ -351,7 +355,7 @@ def main():
             calls.append(pm.prepare_mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt,
                                                      max_context=inp.max_context,
                                                      out=outs[i % 2], schedule_meta=s_meta,
-                                                     stream=stream))
+                                                     stream=stream, **mx_layout))
 
     def fast_step(i, ev0=None, ev1=None):
         if args.mode == "schedule":
@@ -411,10 +415,11 @@ def main():
 
     traffic = counter_traffic(args.workload)
     positions = inp.kv_positions()
-    bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes, inp.head_dim)
+    bpp = algorithmic_bytes_per_position(inp.variant, inp.next_n, out_bytes, inp.head_dim,
+                                         inp.sf_vec_size)
     slots = launch_slots(inp.variant, inp.next_n, inp.num_heads, inp.head_dim)
     lbpp = launch_bytes_per_position(inp.variant, inp.next_n, out_bytes, inp.num_heads,
-                                     inp.head_dim)
+                                     inp.head_dim, inp.sf_vec_size)
     alg_bytes = positions * bpp
     # roofline of the logits kernel: algorithmic bytes of every launch of a
     # call (each launch reads the keys) over the call's duration, i.e. the
@@ -461,6 +466,8 @@ def main():
             "schedule": args.mode, "kv_replicas": R, "units": U,
             "products": ("f16 MFMA of exactly widened e4m3, fp32 sums" if inp.variant == "fp8"
                          else "scaled e2m1 MFMA, fp32 sums"),
+            **({} if inp.variant == "fp8" else {
+                "sf_vec_size": inp.sf_vec_size, "kv_sf_interleaved": inp.kv_sf_interleaved}),
             "timing": ("graph of the %d steps, events around one replay" % K if args.graph else
                        "host launches of prepared calls, " +
                        ("events around every launch" if args.launch_events else

@@ -119,11 +119,19 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
  *
  *   q            packed e2m1 [batch, next_n, 64, 64] (two values per byte, the
  *                even element in the low nibble), 16-B aligned.
- *   q_sf         e8m0 [batch, next_n, 64, 128/sf_vec_size]; sf_vec_size == 32.
+ *   sf_vec_size  32 or 16: values per e8m0 scale code, along head_dim, for
+ *                query and keys alike (other values -> UNSUPPORTED).  The
+ *                pages leave 16 open; this library reads it as one code per
+ *                16 consecutive values, the codes of a row in order.
+ *   q_sf         e8m0 [batch, next_n, 64, 128/sf_vec_size], contiguous.
  *   is_kv_sf_interleaved  0: each page holds 64 x 64 packed key bytes, then
- *                64 x 4 e8m0 scale codes (token-major).  1 -> UNSUPPORTED.
- *   kv_fused     page i at kv_fused + i*page_stride; page_stride >= 4352, a
- *                multiple of 16.
+ *                64 x 128/sf_vec_size codes (token-major).  1: each page
+ *                holds 64 token records, a token's 64 packed bytes followed
+ *                by its 128/sf_vec_size codes (records of 68 or 72 bytes; the
+ *                pages name the flag without its layout, this is the reading
+ *                taken).  Other values -> UNSUPPORTED.
+ *   kv_fused     page i at kv_fused + i*page_stride; page_stride >=
+ *                64 * (64 + 128/sf_vec_size) (4352 or 4608), a multiple of 16.
  *   out_dtype    PMQA_BF16 (the default of this variant, round to nearest even)
  *                or PMQA_F32.  The e2m1 products and their block scales are
  *                exact on the matrix unit and blocks add at fp32 precision.

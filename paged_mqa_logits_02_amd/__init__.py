@@ -362,13 +362,17 @@ def _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n, sf_ve
     B, N, H, Dh = q.shape
     if next_n is not None and next_n != N:
         raise ValueError("next_n does not match q")
+    if sf_vec_size not in (16, 32):
+        raise ValueError("sf_vec_size must be 16 or 32, got %r" % (sf_vec_size,))
+    if is_kv_sf_interleaved not in (0, 1, False, True):
+        raise ValueError("is_kv_sf_interleaved must be a bool, got %r" % (is_kv_sf_interleaved,))
     _need(q_sf, "q_sf", (torch.uint8, torch.int8, torch.float8_e8m0fnu), 4)
-    if tuple(q_sf.shape[:3]) != (B, N, H) or q_sf.shape[3] * max(sf_vec_size, 1) != 2 * Dh:
+    if tuple(q_sf.shape[:3]) != (B, N, H) or q_sf.shape[3] * sf_vec_size != 2 * Dh:
         raise ValueError("q_sf has shape %s; expected [%d, %d, %d, %d]" % (
-            tuple(q_sf.shape), B, N, H, 2 * Dh // max(sf_vec_size, 1)))
+            tuple(q_sf.shape), B, N, H, 2 * Dh // sf_vec_size))
     _need_contiguous(q_sf, "q_sf")
     _check_mqa(q, q_sf, kv_fused, weights, seq_lens, block_table, out, schedule_meta,
-               PAGE * (Dh + 2 * Dh // 32), Dh)
+               PAGE * (Dh + 2 * Dh // sf_vec_size), Dh)
     bt_stride, bt_width = _rows_of(block_table)
     if max_context is None:
         max_context = out.shape[1] if out is not None else bt_width * PAGE
@@ -387,9 +391,12 @@ def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=N
                      schedule_meta=None, output_dtype=torch.bfloat16, stream=None):
     """MXFP4 paged MQA logits; returns ``out`` [batch*next_n, max_context].
 
-    q [batch, next_n, 64, 64] packed e2m1 uint8; q_sf [batch, next_n, 64, 4]
-    e8m0 uint8; kv_fused [pages, page_bytes] uint8 with 64x64 packed key bytes
-    then 64x4 e8m0 codes per page."""
+    q [batch, next_n, 64, 64] packed e2m1 uint8; q_sf [batch, next_n, 64,
+    128 // sf_vec_size] e8m0 uint8 (sf_vec_size 32 or 16 values per code);
+    kv_fused [pages, page_bytes] uint8.  A page holds 64 tokens: with
+    is_kv_sf_interleaved False, 64x64 packed key bytes then 64 x (128 //
+    sf_vec_size) e8m0 codes; with True, 64 records of a token's 64 packed
+    bytes followed by its codes."""
     out, args = _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n,
                             sf_vec_size, is_kv_sf_interleaved, max_context, out, schedule_meta,
                             output_dtype, stream)

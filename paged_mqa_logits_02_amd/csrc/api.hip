@@ -15,11 +15,11 @@ struct DeviceInfo {
   bool ready = false;
   int cus = 0;
   size_t lds_per_cu = 0;
-  // workgroups per CU of each 64-head kernel instance [slots-1][variant][out]
-  // and of each general FP8 instance [ks-1][out], from registers alone, and
-  // each instance's static LDS bytes
-  int occ[kFastSlots][2][2] = {};
-  size_t static_lds[kFastSlots][2][2] = {};
+  // workgroups per CU of each 64-head kernel instance [slots-1][kernel
+  // variant][out] and of each general FP8 instance [ks-1][out], from registers
+  // alone, and each instance's static LDS bytes
+  int occ[kFastSlots][kKernelVariants][2] = {};
+  size_t static_lds[kFastSlots][kKernelVariants][2] = {};
   int occ_any[2][2] = {};
   size_t static_lds_any[2][2] = {};
 };
@@ -79,7 +79,7 @@ int init_device(int device) {
     // occupancy from registers (LDS is accounted per call: it depends on
     // the batch and the shape)
     for (int n = 1; n <= kFastSlots && rc == PMQA_OK; ++n)
-      for (int v = 0; v < 2 && rc == PMQA_OK; ++v)
+      for (int v = 0; v < kKernelVariants && rc == PMQA_OK; ++v)
         for (int o = 0; o < 2 && rc == PMQA_OK; ++o)
           if (!query_kernel(mqa_kernel_symbol(n, v, o), &d.occ[n - 1][v][o],
                             &d.static_lds[n - 1][v][o]))
@@ -232,16 +232,18 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
                      const int32_t* schedule, void* stream) {
   if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
   if (num_heads != 64 || head_dim != 128) return PMQA_ERR_UNSUPPORTED;
-  if (sf_vec_size != 32 || is_kv_sf_interleaved != 0) return PMQA_ERR_UNSUPPORTED;
+  if (sf_vec_size != 16 && sf_vec_size != 32) return PMQA_ERR_UNSUPPORTED;
+  if (is_kv_sf_interleaved != 0 && is_kv_sf_interleaved != 1) return PMQA_ERR_UNSUPPORTED;
   if (out_dtype != PMQA_F32 && out_dtype != PMQA_BF16) return PMQA_ERR_UNSUPPORTED;
   int rc = check_mqa_common(q, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
                             bt_stride, bt_width, batch, next_n, out, out_row_stride, max_context,
-                            (int64_t)PMQA_PAGE_TOKENS * (head_dim / 2 + head_dim / 32));
+                            (int64_t)PMQA_PAGE_TOKENS * (head_dim / 2 + head_dim / sf_vec_size));
   if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
   if (!q_sf) return PMQA_ERR_NULL;
   return run_mqa(q, q_sf, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
-                 bt_stride, batch, next_n, num_heads, head_dim, PMQA_VARIANT_MXFP4, out,
-                 out_row_stride, max_context, out_dtype, schedule, stream);
+                 bt_stride, batch, next_n, num_heads, head_dim,
+                 mx_kernel_variant(sf_vec_size, is_kv_sf_interleaved), out, out_row_stride,
+                 max_context, out_dtype, schedule, stream);
 }
 
 // Validation shared by both indexer entry points; key_bytes is the packed size

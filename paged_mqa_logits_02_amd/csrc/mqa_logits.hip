@@ -32,6 +32,9 @@
 // can lose the whole value of a cancelling dot product.  MXFP4 operands are
 // multiplied as they are with the scaled f8f6f4 instruction: an e2m1 product
 // always fits that window, so those sums are exact.
+#include <type_traits>
+#include <utility>
+
 #include "ring.hpp"
 
 namespace pmqa {
@@ -66,48 +69,133 @@ __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------- MXFP4 page and operands
+//
+// Kernel variants: 0 is FP8; 1..4 are MXFP4 with a scale layout ("flashinfer.
+// attn_scores", paragraph on how the variants differ: q_sf, sf_vec_size and
+// is_kv_sf_interleaved): 1 = one e8m0 code per 32 values, codes after all
+// packed rows; 2 = one code per 16 values, codes after all packed rows; 3 and
+// 4 = the same with each token's codes right after its packed bytes (64
+// records per page).
+__host__ __device__ constexpr int mx_sfv(int var) { return var == 2 || var == 4 ? 16 : 32; }
+__host__ __device__ constexpr bool mx_records(int var) { return var >= 3; }
+constexpr int kMxVariants = 4;
 
-template <> struct PageLayout<1> {       // MXFP4: 64 x 64 B packed keys, 64 x 4 e8m0
+// An MXFP4 page in LDS always has the same image, whatever its layout in
+// memory: 64 packed rows of 64 bytes (16-byte chunks XOR-permuted by row, as
+// for FP8), then the 64 tokens' codes, kCodes per token.  With trailing codes
+// a wave loads its 16 rows as one 16-byte piece per lane and its tokens'
+// codes as dwords; with token records it gathers the same bytes with dword
+// loads from each record (4-byte aligned: a record is 68 or 72 bytes).
+template <int SFV, bool REC> struct MxPageLayout {
   static constexpr int kRowBytes = 64;
   static constexpr int kKeyBytes = kPage * kRowBytes;  // 4096
-  static constexpr int kStageBytes = kKeyBytes + kPage * 4;
-  static constexpr int kLoadsPerWave = 2;
+  static constexpr int kCodes = 128 / SFV;             // e8m0 codes per token
+  static constexpr int kStageBytes = kKeyBytes + kPage * kCodes;
+  static constexpr int kRecBytes = kRowBytes + kCodes;  // a token record
+  static constexpr int kCodeDwords = 16 * kCodes / 4;   // a wave's tokens' codes
+  static constexpr int kLoadsPerWave = REC ? 5 : 2;
   __device__ static int swz(int r) { return (r >> 1) & 3; }
   struct Lanes {
-    uint32_t key;
-    uint32_t scale;
+    uint32_t off[kLoadsPerWave];
   };
+  // Wave w loads rows 16w .. 16w+15 and those tokens' codes.
   __device__ static Lanes lanes(int wave, int lane) {
-    const int r = 16 * wave + (lane >> 2);
     Lanes o;
-    o.key = r * kRowBytes + 16 * ((lane & 3) ^ swz(r));
-    o.scale = kKeyBytes + 64 * wave + 4 * (lane & 15);
+    if constexpr (!REC) {
+      const int r = 16 * wave + (lane >> 2);
+      o.off[0] = r * kRowBytes + 16 * ((lane & 3) ^ swz(r));
+      o.off[1] = kKeyBytes + 16 * wave * kCodes + 4 * (lane < kCodeDwords ? lane : 0);
+    } else {
+      // load k of the wave's rows: LDS dword 64k + lane of its 1 KB block is
+      // byte 4e of slot s of row rr, which holds chunk s ^ swz(r) of the row
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d = 64 * k + lane, rr = d >> 4, s = (d >> 2) & 3, e = d & 3;
+        const int r = 16 * wave + rr;
+        o.off[k] = r * kRecBytes + 16 * (s ^ swz(r)) + 4 * e;
+      }
+      const int c = lane < kCodeDwords ? lane : 0;  // code dword c of the wave's tokens
+      const int r = 16 * wave + c / (kCodes / 4);
+      o.off[4] = r * kRecBytes + kRowBytes + 4 * (c % (kCodes / 4));
+    }
     return o;
   }
   __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
                                int lane) {
-    dma16_page(page + o.key, stage + 16 * wave * kRowBytes);
-    if (lane < 16) dma4_page(page + o.scale, stage + kKeyBytes + 64 * wave);
+    if constexpr (!REC) {
+      dma16_page(page + o.off[0], stage + 16 * wave * kRowBytes);
+      if (lane < kCodeDwords) dma4_page(page + o.off[1], stage + kKeyBytes + 16 * wave * kCodes);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dma4_page(page + o.off[k], stage + 16 * wave * kRowBytes + 256 * k);
+      if (lane < kCodeDwords) dma4_page(page + o.off[4], stage + kKeyBytes + 16 * wave * kCodes);
+    }
   }
 };
+template <> struct PageLayout<1> : MxPageLayout<32, false> {};
+template <> struct PageLayout<2> : MxPageLayout<16, false> {};
+template <> struct PageLayout<3> : MxPageLayout<32, true> {};
+template <> struct PageLayout<4> : MxPageLayout<16, true> {};
 
-// MXFP4: lane l holds the 32-element block g = l>>4 (16 packed bytes) and that
-// block's e8m0 code.
-template <> struct Frag<1> {
+// MXFP4 operand fragment (16x16x128 tiles): lane l holds the 32-element block
+// g = l>>4 of its row (16 packed bytes) and its codes: one (sf) per 32 values,
+// or one per 16 (sf for the first half, sf2 for the second).
+template <int SFV> struct MxFrag {
+  static constexpr int kCodes = 128 / SFV;
   v4i v;
-  int sf;
+  int sf, sf2;
   __device__ __forceinline__ void load_global(const uint8_t* row, int g) {
     v = ldg_untracked(row + 16 * g);
   }
+  // codes of a query row (q_sf row of kCodes codes), loaded with it
+  __device__ __forceinline__ void load_codes_global(const uint8_t* codes, int g) {
+    sf = ldg_untracked_u8(codes + (SFV == 32 ? g : 2 * g));
+    if constexpr (SFV == 16) sf2 = ldg_untracked_u8(codes + 2 * g + 1);
+  }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
-    const int sw = PageLayout<1>::swz(r);
-    v = *reinterpret_cast<const v4i*>(stage + r * PageLayout<1>::kRowBytes + 16 * (g ^ sw));
-    sf = stage[PageLayout<1>::kKeyBytes + r * 4 + g];
+    using L = MxPageLayout<SFV, false>;
+    v = *reinterpret_cast<const v4i*>(stage + r * L::kRowBytes + 16 * (g ^ L::swz(r)));
+    const uint8_t* codes = stage + L::kKeyBytes + r * kCodes;
+    sf = codes[SFV == 32 ? g : 2 * g];
+    if constexpr (SFV == 16) sf2 = codes[2 * g + 1];
+  }
+  __device__ __forceinline__ void settle_codes() {
+    settle(sf);
+    if constexpr (SFV == 16) settle(sf2);
   }
 };
+template <> struct Frag<1> : MxFrag<32> {};
+template <> struct Frag<2> : MxFrag<16> {};
+template <> struct Frag<3> : MxFrag<32> {};
+template <> struct Frag<4> : MxFrag<16> {};
 
-__device__ __forceinline__ v4f mma(const Frag<1>& q, const Frag<1>& k) {
+// Operands of the MXFP4 products.  A key fragment is multiplied as loaded.  A
+// query fragment with one code per 32 values is too; with one code per 16
+// values (the matrix unit takes one code per 32 values of a lane) it is split
+// once per request into its two halves, each with the other half zeroed and
+// its own code: the product is the sum of two scaled products, the whole key
+// fragment with the first half's code, then with the second half's (the
+// zeroed query half removes the key half that the code does not belong to).
+// Both forms are exact: the scaled FP4 products sum without loss.
+struct MxSplitQuery {
+  v4i lo, hi;
+  int sf, sf2;
+};
+template <class F>
+__device__ __forceinline__ MxSplitQuery split_query(const F& f) {
+  return MxSplitQuery{(v4i){f.v[0], f.v[1], 0, 0}, (v4i){0, 0, f.v[2], f.v[3]}, f.sf, f.sf2};
+}
+__device__ __forceinline__ const MxFrag<32>& query_operand(const MxFrag<32>& f) { return f; }
+__device__ __forceinline__ MxSplitQuery query_operand(const MxFrag<16>& f) { return split_query(f); }
+template <int SFV>
+__device__ __forceinline__ const MxFrag<SFV>& key_operand(const MxFrag<SFV>& k) { return k; }
+
+__device__ __forceinline__ v4f mma(const MxFrag<32>& q, const MxFrag<32>& k) {
   return mfma_fp4(q.v, q.sf, k.v, k.sf, (v4f){0.f, 0.f, 0.f, 0.f});
+}
+__device__ __forceinline__ v4f mma(const MxSplitQuery& q, const MxFrag<16>& k) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return mfma_fp4(q.hi, q.sf2, k.v, k.sf2, mfma_fp4(q.lo, q.sf, k.v, k.sf, z));
 }
 
 // How the 4 waves of a workgroup share one page: each wave takes TW query
@@ -128,46 +216,63 @@ template <> struct WaveSplit<4> { static constexpr int TW = 1, SW = 4; static co
 // h = l >> 5, in the same slots for the query and the key operand.
 template <int VAR> struct WideFrag;
 
-// MXFP4: lane l holds 32-element block 2ks + h of the row (16 packed bytes)
-// and that block's e8m0 code.
-template <> struct WideFrag<1> {
+// MXFP4: lane l holds 32-element block c = 2ks + h of the row (16 packed bytes)
+// and its code(s), as MxFrag.
+template <int SFV> struct MxWideFrag {
+  static constexpr int kCodes = 128 / SFV;
   v4i v;
-  int sf;
+  int sf, sf2;
   __device__ __forceinline__ void load_global(const uint8_t* row, int ks, int h) {
     v = ldg_untracked(row + 16 * (2 * ks + h));
   }
-  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
+  __device__ __forceinline__ void load_codes_global(const uint8_t* codes, int ks, int h) {
     const int c = 2 * ks + h;
-    v = *reinterpret_cast<const v4i*>(stage + r * PageLayout<1>::kRowBytes +
-                                      16 * (c ^ PageLayout<1>::swz(r)));
-    sf = stage[PageLayout<1>::kKeyBytes + r * 4 + c];
+    sf = ldg_untracked_u8(codes + (SFV == 32 ? c : 2 * c));
+    if constexpr (SFV == 16) sf2 = ldg_untracked_u8(codes + 2 * c + 1);
+  }
+  __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
+    using L = MxPageLayout<SFV, false>;
+    const int c = 2 * ks + h;
+    v = *reinterpret_cast<const v4i*>(stage + r * L::kRowBytes + 16 * (c ^ L::swz(r)));
+    const uint8_t* codes = stage + L::kKeyBytes + r * kCodes;
+    sf = codes[SFV == 32 ? c : 2 * c];
+    if constexpr (SFV == 16) sf2 = codes[2 * c + 1];
+  }
+  __device__ __forceinline__ void settle_codes() {
+    settle(sf);
+    if constexpr (SFV == 16) settle(sf2);
   }
 };
+template <> struct WideFrag<1> : MxWideFrag<32> {};
+template <> struct WideFrag<2> : MxWideFrag<16> {};
+template <> struct WideFrag<3> : MxWideFrag<32> {};
+template <> struct WideFrag<4> : MxWideFrag<16> {};
 
-__device__ __forceinline__ const Frag<1>& key_operand(const Frag<1>& k) { return k; }
-__device__ __forceinline__ v16f mma_wide(const WideFrag<1>& q, const WideFrag<1>& k,
+__device__ __forceinline__ const MxWideFrag<32>& query_operand(const MxWideFrag<32>& f) {
+  return f;
+}
+__device__ __forceinline__ MxSplitQuery query_operand(const MxWideFrag<16>& f) {
+  return split_query(f);
+}
+__device__ __forceinline__ v16f mma_wide(const MxWideFrag<32>& q, const MxWideFrag<32>& k,
                                          const v16f& c) {
   return mfma32_fp4(q.v, q.sf, k.v, k.sf, c);
+}
+__device__ __forceinline__ v16f mma_wide(const MxSplitQuery& q, const MxWideFrag<16>& k,
+                                         const v16f& c) {
+  return mfma32_fp4(q.hi, q.sf2, k.v, k.sf2, mfma32_fp4(q.lo, q.sf, k.v, k.sf, c));
 }
 
 // The query operand of one head tile as the products take it: an FP8
 // fragment widened to f16 once per request (64 VGPRs for the 64 heads of a
-// slot), an MXFP4 fragment as loaded.
-template <int VAR> struct QOperand {
-  using type = typename std::conditional<VAR == 0, Half32, Frag<VAR>>::type;
-  __device__ static type make(const Frag<VAR>& f) {
-    if constexpr (VAR == 0) {
-      return widen32(f.v);
-    } else {
-      return f;
-    }
-  }
-};
+// slot), an MXFP4 fragment as loaded or split (query_operand).
+__device__ __forceinline__ Half32 query_operand(const Frag<0>& f) { return widen32(f.v); }
+template <class F> using QOperandOf = std::decay_t<decltype(query_operand(std::declval<const F&>()))>;
 
 // The wave's query slots of request b (all 64 heads) and their head weights.
 template <int TW, int VAR> struct QueryFrag {
   Frag<VAR> q[4][TW];                               // [head tile][slot], as loaded
-  typename QOperand<VAR>::type op[4][TW];       // as multiplied
+  QOperandOf<Frag<VAR>> op[4][TW];  // as multiplied
   v4f w[4][TW];        // w[mt][t][i] = weight of head 16mt + 4(l>>4) + i
 };
 
@@ -178,9 +283,9 @@ __device__ __forceinline__ void settle_query(QueryFrag<TW, VAR>& qf) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       settle(qf.q[mt][t].v);
-      if constexpr (VAR == 1) settle(qf.q[mt][t].sf);
+      if constexpr (VAR != 0) qf.q[mt][t].settle_codes();
       settle(qf.w[mt][t]);
-      qf.op[mt][t] = QOperand<VAR>::make(qf.q[mt][t]);
+      qf.op[mt][t] = query_operand(qf.q[mt][t]);
     }
 }
 
@@ -195,7 +300,7 @@ __device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs
     for (int mt = 0; mt < 4; ++mt) {
       const long long head_row = (row_of(a, b, t0 + t) * 64 + 16 * mt + r);
       qf.q[mt][t].load_global(a.q + head_row * kQRow, g);
-      if constexpr (VAR == 1) qf.q[mt][t].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+      if constexpr (VAR != 0) qf.q[mt][t].load_codes_global(a.q_sf + head_row * Frag<VAR>::kCodes, g);
       qf.w[mt][t] = __builtin_bit_cast(
           v4f, ldg_untracked(a.w + row_of(a, b, t0 + t) * 64 + 16 * mt + 4 * g));
     }
@@ -206,7 +311,8 @@ __device__ __forceinline__ void load_query(QueryFrag<TW, VAR>& qf, const MqaArgs
 // covers heads 32mt + (l & 31), K step ks; w[mt][u][i] is the weight of head
 // 32mt + 8u + 4(l >> 5) + i, the head of output element 4u + i of tile mt.
 template <int VAR> struct WideQuery {
-  WideFrag<VAR> q[2][2];
+  WideFrag<VAR> q[2][2];                     // as loaded
+  QOperandOf<WideFrag<VAR>> op[2][2];        // as multiplied
   v4f w[2][4];
 };
 
@@ -217,7 +323,8 @@ __device__ __forceinline__ void settle_query(WideQuery<VAR>& qf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       settle(qf.q[mt][ks].v);
-      settle(qf.q[mt][ks].sf);
+      qf.q[mt][ks].settle_codes();
+      qf.op[mt][ks] = query_operand(qf.q[mt][ks]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) settle(qf.w[mt][u]);
@@ -236,7 +343,7 @@ __device__ __forceinline__ void load_query(WideQuery<VAR>& qf, const MqaArgs& a,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       qf.q[mt][ks].load_global(a.q + head_row * kQRow, ks, h);
-      qf.q[mt][ks].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + 2 * ks + h);
+      qf.q[mt][ks].load_codes_global(a.q_sf + head_row * WideFrag<VAR>::kCodes, ks, h);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -350,9 +457,9 @@ __device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8
     // the two head tiles alternate so that no product waits on the one just issued
     v16f acc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.q[mt][0], kf[nt][0], (v16f){});
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.op[mt][0], kf[nt][0], (v16f){});
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.q[mt][1], kf[nt][1], acc[mt]);
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = mma_wide(qf.op[mt][1], kf[nt][1], acc[mt]);
     float s_even = 0.0f, s_odd = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -391,7 +498,7 @@ __device__ __forceinline__ void score_page(const WideQuery<VAR>& qf, const uint8
 // FP8 sums the heads in fp32 for both outputs: its f16 products already keep
 // the matrix unit busiest, and the fp32 sum adds no error.
 template <int N, int VAR, int OUTT> struct HeadSumOnMatrix {
-  static constexpr bool value = OUTT == 1 && VAR == 1;
+  static constexpr bool value = OUTT == 1 && VAR != 0;
 };
 
 // The wave's TW slots of request b: each slot's query in four head tiles and
@@ -400,8 +507,9 @@ template <int N, int VAR, int OUTT> struct HeadSumOnMatrix {
 // e <-> head 32s + 16(e >> 2) + 4g + (e & 3), which is where the first stage
 // leaves that head's score in the B operand.
 template <int TW, int VAR> struct RedQuery {
-  static_assert(VAR == 1, "the matrix-unit head sum serves MXFP4");
-  Frag<VAR> q[4][TW];  // [head tile][slot]
+  static_assert(VAR != 0, "the matrix-unit head sum serves MXFP4");
+  Frag<VAR> q[4][TW];                 // [head tile][slot], as loaded
+  QOperandOf<Frag<VAR>> op[4][TW];    // as multiplied
   v4f wraw[TW][2][2];  // [slot][K step][head tile within the step]: as loaded
   v8bf wa[TW][2];      // [slot][K step]: A operand, nonzero in row `slot` only
 };
@@ -414,7 +522,8 @@ __device__ __forceinline__ void settle_query(RedQuery<TW, VAR>& qf) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       settle(qf.q[mt][t].v);
-      settle(qf.q[mt][t].sf);
+      qf.q[mt][t].settle_codes();
+      qf.op[mt][t] = query_operand(qf.q[mt][t]);
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -439,7 +548,7 @@ __device__ __forceinline__ void load_red_query(RedQuery<TW, VAR>& qf, const MqaA
     for (int mt = 0; mt < 4; ++mt) {
       const long long head_row = slot * 64 + 16 * mt + r;
       qf.q[mt][t].load_global(a.q + head_row * 64, g);
-      qf.q[mt][t].sf = ldg_untracked_u8(a.q_sf + head_row * 4 + g);
+      qf.q[mt][t].load_codes_global(a.q_sf + head_row * Frag<VAR>::kCodes, g);
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -450,26 +559,29 @@ __device__ __forceinline__ void load_red_query(RedQuery<TW, VAR>& qf, const MqaA
   }
 }
 
-// MXFP4: the lane's key and scale addresses of sub-tile 0 (rows from
-// 16 s0), computed once per page; sub-tile s adds s * 1024 / s * 64.  The
+// MXFP4: the lane's key and code addresses of sub-tile 0 (rows from 16 s0),
+// computed once per page; sub-tile s adds s * 1024 / s * 16 * kCodes.  The
 // empty asm makes the two bases opaque, so the compiler keeps them as bases
 // with the sub-tile constant in the offset field (rather than hoisting one
 // lane offset per sub-tile and adding the page base to each).
+template <int VAR>
 struct Fp4SubtileBase {
+  using L = PageLayout<VAR>;
+  static constexpr int kCodes = L::kCodes;
   typedef __attribute__((address_space(3))) const uint8_t* lds_ptr;
   lds_ptr key, scale;
   __device__ __forceinline__ Fp4SubtileBase(const uint8_t* stage, int s0, int rr, int g) {
-    using L = PageLayout<1>;
     const lds_ptr st = (lds_ptr)stage;
     key = st + (16 * s0 + rr) * L::kRowBytes + 16 * (g ^ L::swz(rr));
-    scale = st + L::kKeyBytes + (16 * s0 + rr) * 4 + g;
+    scale = st + L::kKeyBytes + (16 * s0 + rr) * kCodes + (kCodes == 4 ? g : 2 * g);
     asm("" : "+v"(key));
     asm("" : "+v"(scale));
   }
-  __device__ __forceinline__ void load(Frag<1>& f, int s) const {
+  __device__ __forceinline__ void load(Frag<VAR>& f, int s) const {
     f.v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
-        key + 16 * s * PageLayout<1>::kRowBytes);
-    f.sf = scale[16 * s * 4];
+        key + 16 * s * L::kRowBytes);
+    f.sf = scale[16 * s * kCodes];
+    if constexpr (kCodes == 8) f.sf2 = scale[16 * s * kCodes + 1];
   }
 };
 
@@ -495,7 +607,7 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
   const int g = lane >> 4, rr = lane & 15;
   const long long col0 = (long long)j * kPage;
   Frag<VAR> kf[SW];
-  const Fp4SubtileBase base(stage, s0, rr, g);
+  const Fp4SubtileBase<VAR> base(stage, s0, rr, g);
 #pragma unroll
   for (int si = 0; si < SW; ++si) base.load(kf[si], si);
   // All sub-tiles first (no store, hence no branch, in between, so the
@@ -508,7 +620,7 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
     for (int t = 0; t < TW; ++t) {
       v4f acc[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = mma(qf.q[mt][t], kf[si]);
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = mma(qf.op[mt][t], kf[si]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const v4f& lo = acc[2 * st];
@@ -548,7 +660,7 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
 template <bool Wide, int N, int VAR> struct QueryPick { using type = QueryFrag<WaveSplit<N>::TW, VAR>; };
 template <int N, int VAR> struct QueryPick<true, N, VAR> { using type = WideQuery<VAR>; };
 template <int N, int VAR, int OUTT, bool Red = HeadSumOnMatrix<N, VAR, OUTT>::value>
-struct QueryOf : QueryPick<WaveSplit<N>::kWide && VAR == 1, N, VAR> {};
+struct QueryOf : QueryPick<WaveSplit<N>::kWide && VAR != 0, N, VAR> {};
 template <int N, int VAR, int OUTT> struct QueryOf<N, VAR, OUTT, true> {
   using type = RedQuery<WaveSplit<N>::TW, VAR>;
 };
@@ -738,7 +850,7 @@ __global__ void __launch_bounds__(256)
   bool use_sched = false;
   if (sc != nullptr) {
     const int h0 = sc[0], h1 = sc[1], h2 = sc[2], h3 = sc[3], h4 = sc[4], h5 = sc[5], h6 = sc[6];
-    use_sched = (h0 == kSchedMagic) & (h2 == a.next_n) & (h3 == VAR) & (h4 == a.max_context) &
+    use_sched = (h0 == kSchedMagic) & (h2 == a.next_n) & (h3 == (VAR == 0 ? 0 : 1)) & (h4 == a.max_context) &
                 (h5 == a.batch) & (h6 == s_prefix[a.batch]) & (h1 > 0);
   }
   if (use_sched) {
@@ -767,23 +879,43 @@ static const void* kernel_ptr() {
   return reinterpret_cast<const void*>(&mqa_logits_kernel<N, VAR, OUTT>);
 }
 
-const void* mqa_kernel_symbol(int slots, int variant, int out_dtype) {
-#define PMQA_K(n)                                                                         \
-  if (slots == n) {                                                                       \
-    if (variant == 0) return out_dtype == 0 ? kernel_ptr<n, 0, 0>() : kernel_ptr<n, 0, 1>(); \
-    return out_dtype == 0 ? kernel_ptr<n, 1, 0>() : kernel_ptr<n, 1, 1>();               \
+template <int N, int VAR>
+static const void* kernel_ptr(int out_dtype) {
+  return out_dtype == 0 ? kernel_ptr<N, VAR, 0>() : kernel_ptr<N, VAR, 1>();
+}
+
+template <int N>
+static const void* kernel_ptr(int variant, int out_dtype) {
+  switch (variant) {
+    case 0: return kernel_ptr<N, 0>(out_dtype);
+    case 1: return kernel_ptr<N, 1>(out_dtype);
+    case 2: return kernel_ptr<N, 2>(out_dtype);
+    case 3: return kernel_ptr<N, 3>(out_dtype);
+    case 4: return kernel_ptr<N, 4>(out_dtype);
+    default: return nullptr;
   }
-  PMQA_K(1)
-  PMQA_K(2)
-  PMQA_K(3)
-  PMQA_K(4)
-#undef PMQA_K
-  return nullptr;
+}
+
+const void* mqa_kernel_symbol(int slots, int variant, int out_dtype) {
+  switch (slots) {
+    case 1: return kernel_ptr<1>(variant, out_dtype);
+    case 2: return kernel_ptr<2>(variant, out_dtype);
+    case 3: return kernel_ptr<3>(variant, out_dtype);
+    case 4: return kernel_ptr<4>(variant, out_dtype);
+    default: return nullptr;
+  }
 }
 
 size_t mqa_ring_bytes(int variant, int slots) {
   (void)slots;
-  return variant == 0 ? (size_t)ring_bytes<1, 0>() : (size_t)ring_bytes<1, 1>();
+  switch (variant) {
+    case 0: return ring_bytes<1, 0>();
+    case 1: return ring_bytes<1, 1>();
+    case 2: return ring_bytes<1, 2>();
+    case 3: return ring_bytes<1, 3>();
+    case 4: return ring_bytes<1, 4>();
+    default: return 0;
+  }
 }
 
 hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, int grid,

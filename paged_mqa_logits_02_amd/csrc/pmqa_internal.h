@@ -14,7 +14,7 @@ constexpr int kMaxBatch = 8192;           // prefix of page counts kept in LDS
 // Arguments of the MQA logits kernels (FP8 and MXFP4).
 struct MqaArgs {
   const uint8_t* q;        // fp8 [B,N,H,D] or packed fp4 [B,N,64,64]
-  const uint8_t* q_sf;     // e8m0 [B,N,64,4] (MXFP4 only)
+  const uint8_t* q_sf;     // e8m0 [B,N,64,128/sf_vec_size] (MXFP4 only)
   const uint8_t* kv;       // pages
   long long page_stride;   // bytes between pages
   const float* w;          // [B*N, H]
@@ -59,8 +59,14 @@ struct IdxArgs {
 };
 
 // Kernels for 64 heads and head_dim 128, one instance per slot count of a
-// pass (1..kFastSlots).
+// pass (1..kFastSlots) and kernel variant: 0 is FP8; 1..4 are MXFP4 with
+// one e8m0 code per sf_vec_size values (32 or 16), the key codes either
+// after all packed rows of a page or right after each token's packed bytes.
 constexpr int kFastSlots = 4;
+constexpr int kKernelVariants = 5;
+inline int mx_kernel_variant(int sf_vec_size, int kv_sf_interleaved) {
+  return 1 + (sf_vec_size == 16 ? 1 : 0) + (kv_sf_interleaved ? 2 : 0);
+}
 // Skew of the work split toward early dispatch rounds (1/1024ths) for a
 // launch of `slots` query slots of `variant` (measured: 4 FP8 slots, whose
 // launches are long enough for the rounds to drift apart, gain ~4%).

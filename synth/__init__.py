@@ -363,7 +363,11 @@ def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=409
 
 SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5,
          "indexer_nvfp4": 6, "verify_fp8_n8": 7, "verify_fp8_h32": 8, "verify_fp8_bf16": 4,
-         "mxfp4_n4": 9}
+         "mxfp4_n4": 9, "mxfp4_sf16": 5, "mxfp4_records": 5, "mxfp4_sf16_records": 5}
+
+# the MXFP4 scale layouts of the mxfp4 workload: (sf_vec_size, interleaved)
+MX_LAYOUT_CONFIGS = {"mxfp4": (32, False), "mxfp4_sf16": (16, False),
+                     "mxfp4_records": (32, True), "mxfp4_sf16_records": (16, True)}
 
 
 def _lens(name, rng):
@@ -374,7 +378,7 @@ def _lens(name, rng):
         return rng.integers(4096, 65536 + 1, size=128).astype(np.int32)
     if name == "verify_fp8_n8":
         return rng.integers(4096, 65536 + 1, size=64).astype(np.int32)
-    if name in ("mxfp4", "mxfp4_n4"):
+    if name in ("mxfp4_n4",) or name in MX_LAYOUT_CONFIGS:
         return rng.integers(16384, 131072 + 1, size=64).astype(np.int32)
     raise KeyError(name)
 
@@ -396,6 +400,9 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
                  w ~ N(0, 0.1^2)
     verify_fp8_bf16 verify_fp8 (same seed and lengths) with bf16 out
     mxfp4_n4     B=64, next_n=4, seq_lens uniform in 16K..128K, bf16 out
+    mxfp4_sf16, mxfp4_records, mxfp4_sf16_records
+                 mxfp4 (same seed and lengths) with one code per 16 values,
+                 with each token's codes after its packed bytes, or both
     """
     if seed is None:
         seed = SEEDS[name]
@@ -406,8 +413,8 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
         kw = dict(fmt="bf16" if name == "indexer_bf16" else "nvfp4")
         kw.update(overrides)
         return make_indexer_inputs(seed=seed, name=name, **kw)
-    elif name in ("decode_fp8", "verify_fp8", "mxfp4", "verify_fp8_n8", "verify_fp8_h32",
-                  "verify_fp8_bf16", "mxfp4_n4"):
+    elif name in ("decode_fp8", "verify_fp8", "verify_fp8_n8", "verify_fp8_h32",
+                  "verify_fp8_bf16", "mxfp4_n4") or name in MX_LAYOUT_CONFIGS:
         lens = _lens(name, np.random.default_rng(seed + 1000))
         if name == "decode_fp8":
             kw = dict(seq_lens=lens, next_n=1, max_context=32768, bt_width=512, w_std=0.1)
@@ -425,8 +432,9 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
             kw = dict(seq_lens=lens, next_n=2, max_context=65536, bt_width=1024, w_std=0.1,
                       num_heads=32)
         else:
+            sfv, il = MX_LAYOUT_CONFIGS[name]
             kw = dict(seq_lens=lens, next_n=2, max_context=131072, bt_width=2048, w_std=1.0,
-                      variant="mxfp4")
+                      variant="mxfp4", sf_vec_size=sfv, kv_sf_interleaved=il)
     else:
         raise KeyError(name)
     kw.update(overrides)

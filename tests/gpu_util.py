@@ -62,6 +62,8 @@ class DevMqa:
                              stream=stream)
         else:
             m.mqa_logits_mxfp4(self.q, self.q_sf, self.kv, self.w, self.sl, self.bt,
+                               sf_vec_size=self.inp.sf_vec_size,
+                               is_kv_sf_interleaved=self.inp.kv_sf_interleaved,
                                max_context=self.inp.max_context, out=out,
                                schedule_meta=schedule, stream=stream)
         return out

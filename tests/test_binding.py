@@ -52,7 +52,8 @@ def call_fp8(pm, a):
 
 def call_mxfp4(pm, a):
     pm.mqa_logits_mxfp4(a["q"], a["q_sf"], a["kv_fused"], a["weights"], a["seq_lens"],
-                        a["block_table"], out=a["out"])
+                        a["block_table"], out=a["out"], sf_vec_size=a.get("sf_vec_size", 32),
+                        is_kv_sf_interleaved=a.get("is_kv_sf_interleaved", False))
 
 
 FP8_BAD = {
@@ -97,6 +98,36 @@ MXFP4_BAD = {
 def test_mxfp4_bad_argument_raises(pm, case):
     with pytest.raises(ValueError):
         call_mxfp4(pm, mxfp4_args(**MXFP4_BAD[case]))
+
+
+# (arguments, message): one code per 16 values needs 8 codes per query row and
+# 64 * (64 + 8) bytes per page; other code sizes and flags are refused.
+MXFP4_LAYOUT_BAD = {
+    "sf_vec_size 8": (dict(sf_vec_size=8), "sf_vec_size"),
+    "sf_vec_size 64": (dict(sf_vec_size=64), "sf_vec_size"),
+    "interleaved 2": (dict(is_kv_sf_interleaved=2), "is_kv_sf_interleaved"),
+    "sf16 with 4 codes a row": (dict(sf_vec_size=16), "q_sf"),
+    "sf16 pages of sf32 size": (dict(sf_vec_size=16, q_sf=torch.zeros((B, N, H, 8),
+                                                                        dtype=torch.uint8)),
+                                "kv_fused"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MXFP4_LAYOUT_BAD))
+def test_mxfp4_bad_layout_raises(pm, case):
+    over, msg = MXFP4_LAYOUT_BAD[case]
+    with pytest.raises(ValueError, match=msg):
+        call_mxfp4(pm, mxfp4_args(**over))
+
+
+def test_mxfp4_sf16_records_pass_host_checks(pm):
+    """A well-formed sf_vec_size 16, interleaved call fails only on the device
+    check (CPU tensors here)."""
+    a = mxfp4_args(sf_vec_size=16, is_kv_sf_interleaved=True,
+                   q_sf=torch.zeros((B, N, H, 8), dtype=torch.uint8),
+                   kv_fused=torch.zeros((P, 64 * (D // 2 + D // 16)), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU|device|cuda"):
+        call_mxfp4(pm, a)
 
 
 def indexer_args(**over):

@@ -104,7 +104,9 @@ def _mx(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,rc", [
-    (dict(sfv=16), UNSUP), (dict(inter=1), UNSUP), (dict(H=32), UNSUP), (dict(D=256), UNSUP),
+    (dict(sfv=16), SHAPE), (dict(sfv=16, ps=4608, B=0), OK), (dict(sfv=8), UNSUP),
+    (dict(sfv=64), UNSUP), (dict(sfv=0), UNSUP), (dict(inter=2), UNSUP), (dict(inter=-1), UNSUP),
+    (dict(inter=1, B=0), OK), (dict(H=32), UNSUP), (dict(D=256), UNSUP),
     (dict(qsf=None), NULL), (dict(ps=4340), SHAPE), (dict(ps=4352 + 4), ALIGN),
     (dict(N=9), UNSUP), (dict(B=0), OK),
 ])

@@ -32,9 +32,9 @@ def drains_before_mfma(asm, kernel="17mqa_logits_kernel"):
 
 
 # source, mangled kernel name stem, instances: the 64-head kernels (slots 1..4
-# x {fp8, mxfp4} x {fp32, bf16 out}) and the general FP8 kernels (1 or 2
+# x {fp8, four mxfp4 scale layouts} x {fp32, bf16 out}) and the general FP8 kernels (1 or 2
 # planes x {fp32, bf16 out})
-SOURCES = [("mqa_logits.hip", "17mqa_logits_kernel", 16),
+SOURCES = [("mqa_logits.hip", "17mqa_logits_kernel", 40),
            ("mqa_any.hip", "21mqa_logits_any_kernel", 4)]
 
 
