@@ -1,4 +1,5 @@
-"""CPU oracle for paged MQA logits and one-head indexer scores (float64).
+"""CPU oracle for paged MQA logits, one-head indexer scores and the block-max
+proxy score (float64).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The GPU product path never imports
@@ -17,6 +18,11 @@ Which passage each function follows:
                             "flashinfer.sdsa.indexer_scores": description and
                             parameter list (BF16 inputs; NVFP4 inputs with
                             query_scales / key_scales).
+  * ``proxy_score_fp4_for`` / ``proxy_score_fp4_points_for`` - FlashInfer
+                            "flashinfer.msa_ops.msa_proxy_score_fp4":
+                            description, parameter list and "Returns" (the
+                            readings where it defers to an absent page are
+                            in oracle.c).
   * ``e4m3``/``e2m1``/``e8m0``/``bf16`` - OCP 8-bit FP and OCP MX v1.0
                             format definitions.
 """
@@ -65,6 +71,12 @@ def _load():
                                                   P, P, P, ctypes.c_int]
             lib.oracle_indexer_scores_nvfp4.argtypes = [P, P, I32, I32, P, I64, P, I64, P, I64,
                                                         P, P, P, I32, I32, P, P, P, ctypes.c_int]
+            D = ctypes.c_double
+            proxy = [P, P, I32, I32, I32, P, P, ctypes.c_int, I64, I32, P, P, P, I64, I32, P,
+                     I32, D, D, ctypes.c_int, P, I32, ctypes.c_int]
+            lib.oracle_proxy_score_fp4.argtypes = proxy + [P, P, ctypes.c_int]
+            lib.oracle_proxy_score_fp4_points.argtypes = proxy + [I64, P, P, P, P, P,
+                                                                  ctypes.c_int]
             for f in ("oracle_e4m3", "oracle_e2m1", "oracle_e8m0"):
                 getattr(lib, f).argtypes = [ctypes.c_uint8]
                 getattr(lib, f).restype = ctypes.c_double
@@ -251,6 +263,56 @@ def indexer_scores_for(inp, nthreads=None):
     return indexer_scores(inp.query, inp.key_cache, inp.page_stride, inp.block_table,
                           inp.context_lengths, inp.requests, inp.row_offsets(),
                           inp.max_context, nthreads)
+
+
+# ------------------------------------------------------ block-max proxy score
+
+
+def _proxy_common(inp):
+    q, qs = _c(inp.q, np.uint8), _c(inp.q_scale, np.uint8)
+    k, ks = _c(inp.k, np.uint8), _c(inp.k_scale, np.uint8)
+    cu_q = _c(inp.cu_q, np.int32)
+    cu_k = _c(inp.cu_k, np.int32)
+    pt = _c(inp.page_table, np.int32)
+    su = _c(inp.seqused_k, np.int32)
+    qo = _c(inp.q_offset, np.int32)
+    keep = (q, qs, k, ks, cu_q, cu_k, pt, su, qo)
+    args = [_ptr(q), _ptr(qs), int(q.shape[0]), inp.num_qo_heads, inp.num_kv_heads, _ptr(k),
+            _ptr(ks), int(inp.paged), int(inp.page_stride), int(k.shape[0]) if inp.paged else 0,
+            _ptr(cu_q), _ptr(cu_k), _ptr(pt), int(pt.shape[1]) if pt is not None else 0,
+            int(pt.shape[1]) if pt is not None else 0, _ptr(su), inp.batch,
+            float(inp.q_global_scale), float(inp.k_global_scale), int(inp.causal), _ptr(qo),
+            int(inp.max_k_tiles), int(inp.reduce_heads)]
+    return args, keep
+
+
+def proxy_score_fp4_for(inp, nthreads=None):
+    """Dense oracle of the per-KV-block max proxy score (see oracle.c).
+    Returns (ref, amag), each float64 [H_out, max_k_tiles, total_q]; ref is
+    -inf where a block has no visible key, NaN for an out-of-range page id."""
+    lib = _load()
+    args, keep = _proxy_common(inp)
+    shape = (inp.out_heads, inp.max_k_tiles, inp.total_q)
+    ref = np.empty(shape)
+    amag = np.empty(shape)
+    rc = lib.oracle_proxy_score_fp4(*args, _ptr(ref), _ptr(amag), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_proxy_score_fp4: bad arguments (%d)" % rc)
+    return ref, amag
+
+
+def proxy_score_fp4_points_for(inp, hs, ts, is_, nthreads=None):
+    """The same values at cells (hs[n], ts[n], is_[n])."""
+    lib = _load()
+    args, keep = _proxy_common(inp)
+    hs, ts, is_ = _c(hs, np.int32), _c(ts, np.int32), _c(is_, np.int32)
+    ref = np.empty(hs.shape[0])
+    amag = np.empty(hs.shape[0])
+    rc = lib.oracle_proxy_score_fp4_points(*args, int(hs.shape[0]), _ptr(hs), _ptr(ts), _ptr(is_),
+                                           _ptr(ref), _ptr(amag), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_proxy_score_fp4_points: bad arguments (%d)" % rc)
+    return ref, amag
 
 
 def max_threads() -> int:

@@ -1,5 +1,6 @@
 /*
- * Oracle for paged MQA logits and one-head indexer scores: a plain, slow,
+ * Oracle for paged MQA logits, one-head indexer scores and the block-max
+ * proxy score: a plain, slow,
  * float64 CPU implementation of the definitions.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
@@ -16,6 +17,11 @@
  *                   the output-contract note (unconditional writes within a
  *                   row's scheduled extent; rows of requests with
  *                   seq_lens == 0 are never written).
+ *   [proxy]         "flashinfer.msa_ops.msa_proxy_score_fp4": per-KV-block
+ *                   max of the unscaled, causally masked Q K^T logits with
+ *                   NVFP4 query and keys, global scales folded before the
+ *                   max, output (heads, max_k_tiles, total_q) or (1, ...)
+ *                   with reduce_heads.
  *   [indexer]       "flashinfer.sdsa.indexer_scores": one head, so a score is
  *                   the plain dot product of a query row and a key; pages of
  *                   64 keys; scores[q,k] is written for k below the group's
@@ -453,6 +459,264 @@ int oracle_indexer_scores_nvfp4(const uint8_t* query, const uint8_t* query_scale
                 amag[(int64_t)r * max_context + k] = mag;
                 written[(int64_t)r * max_context + k] = 1;
             }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------- block-max proxy score */
+
+/*
+ * Per-KV-block max of the unscaled, causally masked Q K^T logits with NVFP4
+ * inputs ([proxy] "flashinfer.msa_ops.msa_proxy_score_fp4": description,
+ * parameter list and "Returns").  The page defers most parameters to another
+ * page that is not available; the readings taken here (each listed in the
+ * design notes):
+ *   - head_dim 128 (64 packed bytes per row); each row has 8 e4m3 scales, one
+ *     per 16 values, stored row-major (8 bytes per row) with the page's row
+ *     index: query row = token * Hq + head; flat key row = token * Hkv +
+ *     kv_head; paged key row = (page * Hkv + kv_head) * 128 + token_in_page;
+ *   - a dequantised value is e2m1(nibble) * e4m3(scale of its 16-block); the
+ *     logit of (query token i, head h, key k) is
+ *         (q_global_scale * k_global_scale) * sum_d q[i,h,d] * k[k,kvh,d],
+ *     kvh = h / (Hq / Hkv) (consecutive heads share a KV head), with no other
+ *     scale ("unscaled"); the global scales multiply before the max;
+ *   - a KV block is 128 consecutive keys of a request (the paged K's page):
+ *     block t covers keys 128t .. 128t+127;
+ *   - query token i belongs to request r with cu_q[r] <= i < cu_q[r+1], at
+ *     position p = i - cu_q[r]; Lq = cu_q[r+1] - cu_q[r]; the request's key
+ *     count Lk is cu_k[r+1] - cu_k[r] (flat) or seqused_k[r] (paged, at most
+ *     pt_width * 128); negative counts are 0;
+ *   - causal: key k is visible to token p iff k <= q_offset[r] + p, with
+ *     q_offset[r] defaulting to Lk - Lq (the last query token sees the last
+ *     key); not causal: every key below Lk is visible;
+ *   - out[h, t, i] = max over visible keys k of block t of the logit; -inf
+ *     when block t holds no visible key (past the request's keys, fully
+ *     masked, or token i in no request); a paged block whose page id is
+ *     outside [0, num_pages) is never read, and every output of it that has
+ *     a visible key is NaN;
+ *   - reduce_heads: out[0, t, i] = max over heads of out[h, t, i] (NaN if
+ *     any is NaN).
+ * Output layout [H_out, max_k_tiles, total_q]; amag has the same layout:
+ * the largest |q_global_scale * k_global_scale| * sum_d |q_d k_d| over the
+ * visible keys of the block (0 where the output is -inf or NaN), the
+ * magnitude the parity tolerance scales with.
+ */
+#define PROXY_BLOCK 128
+
+typedef struct {
+    const uint8_t *q, *q_scale, *k, *k_scale;
+    const int32_t *cu_q, *cu_k, *page_table, *seqused_k, *q_offset;
+    int64_t page_stride, pt_stride;
+    int32_t total_q, Hq, Hkv, num_pages, pt_width, B, max_k_tiles;
+    int paged, causal, reduce_heads;
+    double g; /* q_global_scale * k_global_scale */
+} proxy_args;
+
+static double proxy_value(const uint8_t* row, const uint8_t* scales, int d)
+{
+    uint8_t byte = row[d / 2];
+    uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+    return oracle_e2m1(nib) * oracle_e4m3(scales[d / 16]);
+}
+
+/* Key count of request r (reading: at most pt_width blocks when paged). */
+static int64_t proxy_lk(const proxy_args* a, int32_t r)
+{
+    int64_t Lk = a->paged ? a->seqused_k[r] : (int64_t)a->cu_k[r + 1] - a->cu_k[r];
+    if (Lk < 0)
+        Lk = 0;
+    if (a->paged && Lk > (int64_t)a->pt_width * PROXY_BLOCK)
+        Lk = (int64_t)a->pt_width * PROXY_BLOCK;
+    return Lk;
+}
+
+/* Block max of head h over block t for token p of request r: -inf if the
+ * block holds no visible key, NaN if its page id is out of range. */
+static void proxy_cell(const proxy_args* a, int32_t r, int32_t p, int32_t h, int32_t t,
+                       double* val, double* mag)
+{
+    const int64_t Lq = (int64_t)a->cu_q[r + 1] - a->cu_q[r], Lk = proxy_lk(a, r);
+    const int64_t off = a->q_offset ? (int64_t)a->q_offset[r] : Lk - Lq;
+    const int64_t i = (int64_t)a->cu_q[r] + p;
+    const int32_t kvh = h / (a->Hq / a->Hkv);
+    const uint8_t* qrow = a->q + (i * a->Hq + h) * 64;
+    const uint8_t* qsc = a->q_scale + (i * a->Hq + h) * 8;
+    double best = -INFINITY, best_mag = 0.0;
+    int32_t page = 0;
+    int any = 0;
+    int64_t kk;
+    if (a->paged && (int64_t)t * PROXY_BLOCK < Lk)
+        page = a->page_table[(int64_t)r * a->pt_stride + t];
+    for (kk = (int64_t)t * PROXY_BLOCK; kk < (int64_t)(t + 1) * PROXY_BLOCK; ++kk) {
+        const uint8_t *krow, *ksc;
+        double dot = 0.0, m = 0.0;
+        int d;
+        if (kk >= Lk || (a->causal && kk > off + p))
+            continue;
+        any = 1;
+        if (a->paged) {
+            if (page < 0 || page >= a->num_pages)
+                break;
+            krow = a->k + (int64_t)page * a->page_stride +
+                   ((int64_t)kvh * PROXY_BLOCK + kk % PROXY_BLOCK) * 64;
+            ksc = a->k_scale + (((int64_t)page * a->Hkv + kvh) * PROXY_BLOCK + kk % PROXY_BLOCK) * 8;
+        } else {
+            const int64_t row = ((int64_t)a->cu_k[r] + kk) * a->Hkv + kvh;
+            krow = a->k + row * 64;
+            ksc = a->k_scale + row * 8;
+        }
+        for (d = 0; d < 128; ++d) {
+            const double prod = proxy_value(qrow, qsc, d) * proxy_value(krow, ksc, d);
+            dot += prod;
+            m += fabs(prod);
+        }
+        if (a->g * dot > best)
+            best = a->g * dot;
+        if (fabs(a->g) * m > best_mag)
+            best_mag = fabs(a->g) * m;
+    }
+    if (any && a->paged && (page < 0 || page >= a->num_pages)) {
+        *val = NAN;
+        *mag = 0.0;
+        return;
+    }
+    *val = best;
+    *mag = best_mag;
+}
+
+/* Output hout (a head, or 0 with reduce_heads: the max over heads). */
+static void proxy_out(const proxy_args* a, int32_t r, int32_t p, int32_t hout, int32_t t,
+                      double* val, double* mag)
+{
+    int32_t h;
+    if (!a->reduce_heads) {
+        proxy_cell(a, r, p, hout, t, val, mag);
+        return;
+    }
+    *val = -INFINITY;
+    *mag = 0.0;
+    for (h = 0; h < a->Hq; ++h) {
+        double v, m;
+        proxy_cell(a, r, p, h, t, &v, &m);
+        if (isnan(v) || isnan(*val)) {
+            *val = NAN;
+            *mag = 0.0;
+            continue;
+        }
+        if (v > *val)
+            *val = v;
+        if (m > *mag)
+            *mag = m;
+    }
+}
+
+static int proxy_check(const proxy_args* a)
+{
+    int32_t r;
+    if (a->total_q < 0 || a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0 || a->B < 0 ||
+        a->max_k_tiles < 0)
+        return -2;
+    if (a->paged && (a->pt_width < 0 || a->pt_stride < a->pt_width))
+        return -2;
+    for (r = 0; r < a->B; ++r)
+        if (a->cu_q[r] < 0 || a->cu_q[r + 1] < a->cu_q[r] || a->cu_q[r + 1] > a->total_q)
+            return -2;
+    return 0;
+}
+
+static void proxy_fill(proxy_args* a, const uint8_t* q, const uint8_t* q_scale, int32_t total_q,
+                       int32_t Hq, int32_t Hkv, const uint8_t* k, const uint8_t* k_scale,
+                       int paged, int64_t page_stride, int32_t num_pages, const int32_t* cu_q,
+                       const int32_t* cu_k, const int32_t* page_table, int64_t pt_stride,
+                       int32_t pt_width, const int32_t* seqused_k, int32_t B, double qgs,
+                       double kgs, int causal, const int32_t* q_offset, int32_t max_k_tiles,
+                       int reduce_heads)
+{
+    a->q = q, a->q_scale = q_scale, a->k = k, a->k_scale = k_scale;
+    a->cu_q = cu_q, a->cu_k = cu_k, a->page_table = page_table, a->seqused_k = seqused_k;
+    a->q_offset = q_offset;
+    a->page_stride = page_stride, a->pt_stride = pt_stride;
+    a->total_q = total_q, a->Hq = Hq, a->Hkv = Hkv, a->num_pages = num_pages;
+    a->pt_width = pt_width, a->B = B, a->max_k_tiles = max_k_tiles;
+    a->paged = paged, a->causal = causal, a->reduce_heads = reduce_heads;
+    a->g = qgs * kgs;
+}
+
+/* Dense: out and amag are [H_out, max_k_tiles, total_q]. */
+int oracle_proxy_score_fp4(const uint8_t* q, const uint8_t* q_scale, int32_t total_q, int32_t Hq,
+                           int32_t Hkv, const uint8_t* k, const uint8_t* k_scale, int paged,
+                           int64_t page_stride, int32_t num_pages, const int32_t* cu_q,
+                           const int32_t* cu_k, const int32_t* page_table, int64_t pt_stride,
+                           int32_t pt_width, const int32_t* seqused_k, int32_t B, double qgs,
+                           double kgs, int causal, const int32_t* q_offset, int32_t max_k_tiles,
+                           int reduce_heads, double* out, double* amag, int nthreads)
+{
+    proxy_args a;
+    int32_t Hout, r;
+    int64_t idx, plane;
+    proxy_fill(&a, q, q_scale, total_q, Hq, Hkv, k, k_scale, paged, page_stride, num_pages, cu_q,
+               cu_k, page_table, pt_stride, pt_width, seqused_k, B, qgs, kgs, causal, q_offset,
+               max_k_tiles, reduce_heads);
+    if (proxy_check(&a) != 0)
+        return -2;
+    Hout = reduce_heads ? 1 : Hq;
+    plane = (int64_t)max_k_tiles * total_q;
+    for (idx = 0; idx < (int64_t)Hout * plane; ++idx) {
+        out[idx] = -INFINITY; /* tokens in no request */
+        amag[idx] = 0.0;
+    }
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (r = 0; r < B; ++r) {
+        int32_t p, h, t;
+        for (p = 0; p < cu_q[r + 1] - cu_q[r]; ++p)
+            for (h = 0; h < Hout; ++h)
+                for (t = 0; t < max_k_tiles; ++t) {
+                    const int64_t o = ((int64_t)h * max_k_tiles + t) * total_q + cu_q[r] + p;
+                    proxy_out(&a, r, p, h, t, &out[o], &amag[o]);
+                }
+    }
+    return 0;
+}
+
+/* Points (hs[n], ts[n], is[n]): the same values one by one. */
+int oracle_proxy_score_fp4_points(const uint8_t* q, const uint8_t* q_scale, int32_t total_q,
+                                  int32_t Hq, int32_t Hkv, const uint8_t* k,
+                                  const uint8_t* k_scale, int paged, int64_t page_stride,
+                                  int32_t num_pages, const int32_t* cu_q, const int32_t* cu_k,
+                                  const int32_t* page_table, int64_t pt_stride, int32_t pt_width,
+                                  const int32_t* seqused_k, int32_t B, double qgs, double kgs,
+                                  int causal, const int32_t* q_offset, int32_t max_k_tiles,
+                                  int reduce_heads, int64_t npts, const int32_t* hs,
+                                  const int32_t* ts, const int32_t* is, double* out,
+                                  double* amag, int nthreads)
+{
+    proxy_args a;
+    int64_t n;
+    proxy_fill(&a, q, q_scale, total_q, Hq, Hkv, k, k_scale, paged, page_stride, num_pages, cu_q,
+               cu_k, page_table, pt_stride, pt_width, seqused_k, B, qgs, kgs, causal, q_offset,
+               max_k_tiles, reduce_heads);
+    if (proxy_check(&a) != 0)
+        return -2;
+    for (n = 0; n < npts; ++n)
+        if (hs[n] < 0 || hs[n] >= (reduce_heads ? 1 : Hq) || ts[n] < 0 || ts[n] >= max_k_tiles ||
+            is[n] < 0 || is[n] >= total_q)
+            return -2;
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads > 0 ? nthreads : 1)
+    for (n = 0; n < npts; ++n) {
+        int32_t r, found = -1;
+        for (r = 0; r < B; ++r)
+            if (cu_q[r] <= is[n] && is[n] < cu_q[r + 1]) {
+                found = r;
+                break;
+            }
+        if (found < 0) {
+            out[n] = -INFINITY;
+            amag[n] = 0.0;
+        } else {
+            proxy_out(&a, found, is[n] - cu_q[found], hs[n], ts[n], &out[n], &amag[n]);
         }
     }
     return 0;

@@ -358,6 +358,149 @@ def make_indexer_inputs(*, rows=24, num_requests=6, bt_width=64, max_context=409
 
 
 # --------------------------------------------------------------------------
+# block-max proxy score inputs (NVFP4 query and keys)
+# --------------------------------------------------------------------------
+
+PROXY_BLOCK = 128  # keys per KV block (the paged K's page)
+
+
+@dataclasses.dataclass
+class ProxyInputs:
+    q: np.ndarray            # u8 [total_q, Hq, 64] packed e2m1
+    q_scale: np.ndarray      # u8 [total_q * Hq, 8] e4m3, row = token * Hq + head
+    k: np.ndarray            # paged: u8 [num_pages, page_stride]; flat: u8 [total_k, Hkv, 64]
+    k_scale: np.ndarray      # u8 [rows, 8] e4m3 (paged row (page*Hkv + kvh)*128 + token)
+    paged: bool
+    page_stride: int         # paged: bytes between pages (>= Hkv * 128 * 64)
+    cu_q: np.ndarray         # int32 [B+1]
+    cu_k: Optional[np.ndarray]        # flat: int32 [B+1]
+    page_table: Optional[np.ndarray]  # paged: int32 [B, width]
+    seqused_k: Optional[np.ndarray]   # paged: int32 [B]
+    q_global_scale: float
+    k_global_scale: float
+    num_qo_heads: int
+    num_kv_heads: int
+    causal: bool
+    q_offset: Optional[np.ndarray]    # int32 [B] or None (bottom-right default)
+    max_k_tiles: int
+    reduce_heads: bool
+    name: str = ""
+
+    @property
+    def batch(self) -> int:
+        return int(self.cu_q.shape[0]) - 1
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k.shape[0]) if self.paged else 0
+
+    @property
+    def out_heads(self) -> int:
+        return 1 if self.reduce_heads else self.num_qo_heads
+
+    def key_lengths(self) -> np.ndarray:
+        if self.paged:
+            L = np.maximum(self.seqused_k.astype(np.int64), 0)
+            return np.minimum(L, self.page_table.shape[1] * PROXY_BLOCK)
+        return np.maximum(np.diff(self.cu_k.astype(np.int64)), 0)
+
+    def kv_positions(self) -> int:
+        """Keys per KV head summed over requests (block-granular reads)."""
+        L = self.key_lengths()
+        return int(np.sum(np.minimum((L + PROXY_BLOCK - 1) // PROXY_BLOCK, self.max_k_tiles))
+                   * PROXY_BLOCK)
+
+
+def _random_nvfp4_rows(rng, shape_rows, scale_lo=0x30, scale_hi=0x48):
+    """Random packed e2m1 rows (64 bytes) and e4m3 scales (8 per row, codes in
+    [scale_lo, scale_hi): values about 2^-1 .. 2^2): for sizes too large to
+    quantise float data."""
+    packed = rng.integers(0, 256, size=tuple(shape_rows) + (64,), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, size=(int(np.prod(shape_rows)), 8), dtype=np.uint8)
+    return packed, scales
+
+
+def make_proxy_inputs(q_lens, k_lens, *, num_qo_heads=64, num_kv_heads=8, paged=True,
+                      causal=True, q_offset=None, max_k_tiles=None, reduce_heads=False,
+                      pt_width=None, extra_pages=0, page_stride=None, seed=0,
+                      quantize=True, name="") -> ProxyInputs:
+    """One block-max proxy score workload.
+
+    q_lens / k_lens: query tokens and keys per request.  Query rows are N(0,1)
+    data quantised to NVFP4 with a per-tensor global scale 448*6/amax (the
+    inverse is q_global_scale); keys likewise when ``quantize``, else random
+    codes (large workloads).  Paged keys take ceil(L/128) pages per request
+    from a random permutation; unused page-table entries are -1.
+    """
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    k_lens = np.asarray(k_lens, dtype=np.int64)
+    B = int(q_lens.shape[0])
+    Hq, Hkv = int(num_qo_heads), int(num_kv_heads)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    total_q = int(cu_q[-1])
+    xq = rng.standard_normal((total_q, Hq, 128), dtype=np.float32)
+    gq = np.float32(448.0 * 6.0) / np.float32(max(float(np.max(np.abs(xq))), 1e-30))
+    q, qs = quantize_nvfp4(xq * gq)
+    q_scale = qs.reshape(total_q * Hq, 8)
+    q_global = float(np.float32(1.0) / gq)
+    kl = np.maximum(k_lens, 0)
+    blocks = [int((L + PROXY_BLOCK - 1) // PROXY_BLOCK) for L in kl]
+    if max_k_tiles is None:
+        max_k_tiles = max(blocks + [1])
+    k_global = 1.0
+    if paged:
+        if pt_width is None:
+            pt_width = max(blocks + [1])
+        num_pages = max(sum(min(b, pt_width) for b in blocks) + extra_pages, 1)
+        if page_stride is None:
+            page_stride = Hkv * PROXY_BLOCK * 64
+        perm = rng.permutation(num_pages).astype(np.int32)
+        page_table = np.full((B, pt_width), -1, dtype=np.int32)
+        pos = 0
+        for r, T in enumerate(blocks):
+            T = min(T, pt_width)
+            page_table[r, :T] = perm[pos:pos + T]
+            pos += T
+        k = np.zeros((num_pages, page_stride), dtype=np.uint8)
+        if quantize:
+            xk = rng.standard_normal((num_pages, Hkv, PROXY_BLOCK, 128), dtype=np.float32)
+            gk = np.float32(448.0 * 6.0) / np.float32(max(float(np.max(np.abs(xk))), 1e-30))
+            kp, ksc = quantize_nvfp4(xk * gk)
+            k_global = float(np.float32(1.0) / gk)
+        else:
+            kp, ksc = _random_nvfp4_rows(rng, (num_pages, Hkv, PROXY_BLOCK))
+            k_global = 1.0 / 64.0
+        k[:, :Hkv * PROXY_BLOCK * 64] = kp.reshape(num_pages, -1)
+        k_scale = np.ascontiguousarray(ksc.reshape(num_pages * Hkv * PROXY_BLOCK, 8))
+        seqused = k_lens.astype(np.int32)
+        cu_k = None
+    else:
+        cu_k = np.concatenate([[0], np.cumsum(kl)]).astype(np.int32)
+        total_k = int(cu_k[-1])
+        if quantize:
+            xk = rng.standard_normal((total_k, Hkv, 128), dtype=np.float32)
+            gk = np.float32(448.0 * 6.0) / np.float32(max(float(np.max(np.abs(xk))), 1e-30))
+            k, ksc = quantize_nvfp4(xk * gk)
+            k_global = float(np.float32(1.0) / gk)
+        else:
+            k, ksc = _random_nvfp4_rows(rng, (total_k, Hkv))
+            k_global = 1.0 / 64.0
+        k_scale = np.ascontiguousarray(ksc.reshape(total_k * Hkv, 8))
+        page_table = seqused = None
+        page_stride = 0
+    if q_offset is not None:
+        q_offset = np.asarray(q_offset, dtype=np.int32)
+    return ProxyInputs(q, q_scale, k, k_scale, bool(paged), int(page_stride), cu_q, cu_k,
+                       page_table, seqused, q_global, k_global, Hq, Hkv, bool(causal), q_offset,
+                       int(max_k_tiles), bool(reduce_heads), name)
+
+
+# --------------------------------------------------------------------------
 # named workloads
 # --------------------------------------------------------------------------
 

@@ -355,3 +355,70 @@ def cancelling_mqa_inputs(variant, next_n, seed, *, one_hot=True, out_dtype="f32
         inp.kv[:, 64 * D // 2: 64 * D // 2 + 256] = 127
     inp.weights[:] = w
     return inp
+
+
+# ------------------------------------------------------ block-max proxy score
+
+
+def e4m3_code(v):
+    """The e4m3 code of a value the format holds exactly."""
+    c = int(synth.encode_e4m3(np.array([v], dtype=np.float32))[0])
+    assert np_e4m3(np.array([c], np.uint8))[0] == v, "not exact in e4m3: %r" % v
+    return c
+
+
+def proxy_from_case(case):
+    """synth.ProxyInputs from a golden case given as e2m1 values and e4m3 scale
+    values per 16-element block (unlisted: value 0, scale 1.0)."""
+    Hq, Hkv = case["Hq"], case["Hkv"]
+    q_lens = np.array(case["q_lens"], np.int64)
+    k_lens = np.array(case["k_lens"], np.int64)
+    B = len(q_lens)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    total_q = int(cu_q[-1])
+    one = e4m3_code(1.0)
+    qn = np.zeros((total_q, Hq, 128), np.uint8)
+    qs = np.full((total_q, Hq, 8), one, np.uint8)
+    for e in case["queries"]:
+        for d, v in e["v"].items():
+            qn[e["token"], e["head"], int(d)] = e2m1_code(v)
+        for b, v in e.get("sf", {}).items():
+            qs[e["token"], e["head"], int(b)] = e4m3_code(v)
+    pack = lambda n: (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+    if case["paged"]:
+        P = case["num_pages"]
+        pt = np.array(case["page_table"], np.int32)
+        kn = np.zeros((P, Hkv, 128, 128), np.uint8)
+        ks = np.full((P, Hkv, 128, 8), one, np.uint8)
+        for e in case["keys"]:
+            page, tok = pt[e["req"], e["pos"] // 128], e["pos"] % 128
+            for d, v in e["v"].items():
+                kn[page, e["kvh"], tok, int(d)] = e2m1_code(v)
+            for b, v in e.get("sf", {}).items():
+                ks[page, e["kvh"], tok, int(b)] = e4m3_code(v)
+        k = pack(kn).reshape(P, -1).copy()
+        k_scale = ks.reshape(-1, 8).copy()
+        cu_k, seqused, stride = None, k_lens.astype(np.int32), Hkv * 128 * 64
+    else:
+        cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+        kn = np.zeros((int(cu_k[-1]), Hkv, 128), np.uint8)
+        ks = np.full((int(cu_k[-1]), Hkv, 8), one, np.uint8)
+        for e in case["keys"]:
+            row = cu_k[e["req"]] + e["pos"]
+            for d, v in e["v"].items():
+                kn[row, e["kvh"], int(d)] = e2m1_code(v)
+            for b, v in e.get("sf", {}).items():
+                ks[row, e["kvh"], int(b)] = e4m3_code(v)
+        k = pack(kn)
+        k_scale = ks.reshape(-1, 8).copy()
+        pt, seqused, stride = None, None, 0
+    qo = case.get("q_offset")
+    return synth.ProxyInputs(pack(qn), qs.reshape(-1, 8).copy(), k, k_scale, bool(case["paged"]),
+                             stride, cu_q, cu_k, pt, seqused, float(case["q_global_scale"]),
+                             float(case["k_global_scale"]), Hq, Hkv, bool(case["causal"]),
+                             None if qo is None else np.array(qo, np.int32),
+                             int(case["max_k_tiles"]), bool(case["reduce_heads"]), case["name"])
+
+
+def expected_value(v):
+    return -np.inf if v == "-inf" else float(v)
