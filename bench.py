@@ -55,6 +55,10 @@ WORKLOADS = {
     "mxfp4_sf16": "mxfp4 with one e8m0 code per 16 values (8 per token)",
     "mxfp4_records": "mxfp4 with each token's codes after its packed bytes (68-byte records)",
     "mxfp4_sf16_records": "mxfp4 with 8 codes per token in 72-byte token records",
+    "proxy_decode": "block-max proxy score: B=64 x 1 query token, 64 query heads over 8 KV "
+                    "heads, d=128, paged NVFP4 keys (blocks of 128), key counts uniform "
+                    "16K..128K, causal, 1024 blocks per row, fp32 out",
+    "proxy_verify": "proxy_decode with 4 query tokens per request",
     "indexer_bf16": "24 query rows in groups of 1..8 over 6 requests, d=128, bf16 key pages of 64, "
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
     "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "
@@ -257,6 +261,91 @@ def run_indexer(args, torch, synth, pm, dev):
     print(json.dumps(line), flush=True)
 
 
+METRIC_PROXY = ("KV positions/sec (keys of every KV head scored per second), block-max proxy "
+                "score, nvfp4 paged keys, %d query heads over %d KV heads, d=128, MI355X")
+
+
+def proxy_bytes_and_flops(inp):
+    """Algorithmic bytes of one call (every key block scored, once per KV
+    head: 64 packed bytes + 8 e4m3 scales per key; every output float once;
+    the query rows once) and flops (2 * 128 per query head, token and key
+    scored)."""
+    L = inp.key_lengths()
+    lq = np.diff(inp.cu_q).astype(np.int64)
+    blocks = np.minimum((L + 127) // 128, inp.max_k_tiles)
+    keys = blocks * 128  # per KV head, block-granular
+    kb = int(keys.sum()) * inp.num_kv_heads * 72
+    ob = inp.out_heads * inp.max_k_tiles * inp.total_q * 4
+    qb = inp.total_q * inp.num_qo_heads * 72
+    flops = 2.0 * 128 * inp.num_qo_heads * float((lq * keys).sum())
+    return kb + ob + qb, flops, int(keys.sum()) * inp.num_kv_heads
+
+
+def run_proxy(args, torch, synth, pm, dev):
+    """The block-max proxy score workloads: one msa_proxy_score_fp4 call per step."""
+    inp = synth.make_config(args.workload)
+    t = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    raw = t(inp.k)
+    H = inp.num_kv_heads
+    k = raw.as_strided((raw.shape[0], H, 128, 64), (raw.shape[1], 128 * 64, 64, 1))
+    q, qs, ks = t(inp.q), t(inp.q_scale), t(inp.k_scale)
+    cu_q, pt, su = t(inp.cu_q), t(inp.page_table), t(inp.seqused_k)
+    outs = [torch.empty((inp.out_heads, inp.max_k_tiles, inp.total_q), dtype=torch.float32,
+                        device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    maxq = int(np.max(np.diff(inp.cu_q)))
+    calls = [pm.prepare_msa_proxy_score_fp4(q, k, qs, ks, inp.q_global_scale, inp.k_global_scale,
+                                            cu_q, page_table=pt, seqused_k=su,
+                                            causal=inp.causal, max_seqlen_q=maxq,
+                                            max_k_tiles=inp.max_k_tiles, output=outs[i],
+                                            reduce_heads=inp.reduce_heads, stream=stream)
+             for i in range(2)]
+    t_ramp = time.time() + args.ramp
+    i = 0
+    while time.time() < t_ramp:
+        calls[i % 2]()
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
+    for i in range(args.warmup):
+        calls[i % 2]()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        calls[i % 2]()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern = total_ms / K
+    alg, flops, positions = proxy_bytes_and_flops(inp)
+    achieved = alg / (kern * 1e-3) / 1e9
+    tflops = flops / (kern * 1e-3) / 1e12
+    hbm = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    mfma = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
+            "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None}
+    hbm_s, mfma_s = alg / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS["f16"] * 1e12)
+    line = {
+        "metric": METRIC_PROXY % (inp.num_qo_heads, inp.num_kv_heads),
+        "value": positions * K / (total_ms * 1e-3),
+        "unit": "KV positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": kern, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic", "gb_per_s": achieved,
+        "config": {"workload": args.workload, "shape": WORKLOADS[args.workload],
+                   "batch": inp.batch, "total_q": inp.total_q, "pages": inp.num_pages,
+                   "kv_positions": positions, "kernel_ms_avg": kern,
+                   "products": "f16 MFMA of exactly dequantised e2m1 x e4m3, fp32 sums",
+                   "timing": "host launches of prepared calls, events around the %d launches" % K,
+                   "algorithmic_bytes_per_launch": alg, "flops_per_launch": flops,
+                   "hbm": dict(hbm, ideal_us=hbm_s * 1e6), "mfma": dict(mfma, ideal_us=mfma_s * 1e6)},
+        "roofline": mfma if mfma_s > hbm_s else hbm,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +385,9 @@ def main():
     pm.init(0)
     if args.workload.startswith("indexer_"):
         run_indexer(args, torch, synth, pm, dev)
+        return
+    if args.workload.startswith("proxy_"):
+        run_proxy(args, torch, synth, pm, dev)
         return
     inp = synth.make_config(args.workload)
     variant = 0 if inp.variant == "fp8" else 1

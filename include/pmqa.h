@@ -14,6 +14,9 @@
  *   "flashinfer.sdsa.indexer_scores": the one-head case, a plain dot product of
  *   each query row with each key of its request, for groups of 1..8 query rows.
  *
+ *   "flashinfer.msa_ops.msa_proxy_score_fp4": the per-KV-block max of the
+ *   causally masked Q K^T logits with NVFP4 query and keys.
+ *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *     library never reads device memory on the host, never allocates per call,
@@ -209,6 +212,67 @@ int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t ro
                          const int32_t* requests, int32_t groups,
                          const int32_t* group_row_offsets, float* scores,
                          int64_t scores_row_stride, int32_t max_context, void* stream);
+
+/*
+ * msa_proxy_score_fp4 - per-KV-block max of the unscaled, causally masked
+ * Q K^T logits with NVFP4 query and keys.
+ * ("flashinfer.msa_ops.msa_proxy_score_fp4": description, parameter list and
+ * "Returns".  The page defers most parameters to a page that is not
+ * available; the readings taken are stated below.)
+ *
+ *   out[h, t, i] = max over the keys k of block t visible to query token i of
+ *                  g * sum_d q[i, h, d] * k[k, kvh, d],
+ *   g = q_global_scale * k_global_scale (multiplied before the max, as the
+ *   page states), kvh = h / (num_qo_heads / num_kv_heads), block t = keys
+ *   128t .. 128t+127 of token i's request; -inf where block t holds no
+ *   visible key (past the request's keys, fully masked, t at or beyond the
+ *   blocks that exist, or token i in no request).  With reduce_heads != 0
+ *   out[0, t, i] = max over heads.  A dequantised value is e2m1 times the
+ *   e4m3 scale of its 16-value block; products are exact and sums fp32.
+ *
+ *   q_fp4        packed e2m1 [total_q, num_qo_heads, 64] (head_dim 128, even
+ *                element in the low nibble), 16-B aligned.
+ *   q_scale      e4m3 [total_q * num_qo_heads, 8], row token*Hq + head,
+ *                2-B aligned.  (The page's cuBLAS 128x4 tiled scale layout is
+ *                not used: each row's 8 scales are contiguous.)
+ *   k_fp4        paged (page_table != NULL): page i at k_fp4 + i*page_stride
+ *                holds [num_kv_heads, 128, 64] packed bytes; page_stride >=
+ *                num_kv_heads * 8192, a multiple of 16.  Flat (page_table ==
+ *                NULL): [total_k, num_kv_heads, 64].  16-B aligned.
+ *   k_scale      e4m3 rows of 8: paged row (page*Hkv + kv_head)*128 + token
+ *                (num_pages*Hkv*128 rows); flat row token*Hkv + kv_head
+ *                (total_k*Hkv rows).  2-B aligned.
+ *   cu_seqlens_q [batch+1] int32, nondecreasing, cu_seqlens_q[batch] <=
+ *                total_q: request r owns query tokens cu[r] .. cu[r+1]-1.
+ *   cu_seqlens_k flat: [batch+1] int32 key offsets (ignored when paged).
+ *   page_table   paged: [batch, pt_stride] int32, block t of request r is
+ *                page page_table[r*pt_stride + t] (t < pt_width).
+ *   seqused_k    paged: [batch] int32 key counts (at most pt_width*128 are
+ *                used).
+ *   causal       nonzero: key k is visible to the p-th token of its request
+ *                iff k <= q_offset[r] + p; zero: every key is visible.
+ *   q_offset     NULL (default Lk - Lq per request: the last query token sees
+ *                the last key) or [batch] int32.
+ *   max_seqlen_q the longest request's token count, or 0 (unknown: total_q);
+ *                used to choose the kernel instance, never to clamp.
+ *   max_k_tiles  blocks per output row (>= 0).
+ *   out          float32 [reduce_heads ? 1 : num_qo_heads, max_k_tiles,
+ *                total_q], contiguous, 4-B aligned; every element is written.
+ *   Supported: num_qo_heads a multiple of num_kv_heads with at most 64 query
+ *   heads per KV head, batch <= 4096, num_kv_heads * total_q * max_k_tiles
+ *   < 2^31 (otherwise UNSUPPORTED).  A page id outside [0, num_pages) or a
+ *   flat request whose keys lie outside [0, total_k) is never read: its
+ *   blocks' outputs are NaN where a key would be visible.
+ */
+int msa_proxy_score_fp4(const void* q_fp4, const void* q_scale, int32_t total_q,
+                        int32_t num_qo_heads, const void* k_fp4, const void* k_scale,
+                        int32_t num_kv_heads, int64_t page_stride, int32_t num_pages,
+                        int64_t total_k, float q_global_scale, float k_global_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* page_table, int64_t pt_stride, int32_t pt_width,
+                        const int32_t* seqused_k, int32_t batch, int32_t causal,
+                        const int32_t* q_offset, int32_t max_seqlen_q, int32_t max_k_tiles,
+                        int32_t reduce_heads, float* out, void* stream);
 
 /*
  * mqa_logits_schedule - the per-call work split, computed on the GPU.

@@ -55,6 +55,9 @@ def _load():
                                    I64, I32, P]
     lib.indexer_scores_nvfp4.argtypes = [P, P, I32, I32, P, I64, P, I64, I32, P, I64, I32, I32,
                                          P, P, I32, P, P, I64, I32, P]
+    F32 = ctypes.c_float
+    lib.msa_proxy_score_fp4.argtypes = [P, P, I32, I32, P, P, I32, I64, I32, I64, F32, F32, P, P,
+                                        P, I64, I32, P, I32, I32, P, I32, I32, I32, P, P]
     lib.mqa_logits_schedule.argtypes = [P, I32, I32, I32, I32, I32, P, P]
     lib.mqa_logits_schedule_ints.argtypes = [I32]
     lib.mqa_logits_schedule_ints.restype = I64
@@ -68,7 +71,7 @@ def _load():
     lib.mqa_logits_status_string.argtypes = [ctypes.c_int]
     lib.mqa_logits_status_string.restype = ctypes.c_char_p
     for f in ("mqa_logits_fp8", "mqa_logits_mxfp4", "indexer_scores", "mqa_logits_schedule",
-              "mqa_logits_init"):
+              "mqa_logits_init", "msa_proxy_score_fp4"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -525,6 +528,129 @@ def _indexer_args(query, key_cache, block_table, context_lengths, requests, scor
     return (_lib.indexer_scores_nvfp4,
             (_ptr(query), _ptr(query_scales), rows, 2 * half, _ptr(key_cache), ps,
              _ptr(key_scales), sps, npages) + common, "indexer_scores_nvfp4")
+
+
+def _proxy_args(q_fp4, k_fp4, q_scale, k_scale, q_global_scale, k_global_scale, cu_seqlens_q,
+                cu_seqlens_k, page_table, seqused_k, causal, max_seqlen_q, max_k_tiles, output,
+                reduce_heads, q_offset, stream):
+    _need(q_fp4, "q_fp4", (torch.uint8, torch.int8), 3)
+    _need_contiguous(q_fp4, "q_fp4")
+    total_q, hq, half = q_fp4.shape
+    if half != 64:
+        raise ValueError("q_fp4 rows hold %d bytes; head_dim 128 needs 64" % half)
+    _need(q_scale, "q_scale", _BYTE_DTYPES)
+    _need_numel(q_scale, "q_scale", total_q * hq * 8)
+    _need_contiguous(q_scale, "q_scale")
+    _need(k_fp4, "k_fp4", (torch.uint8, torch.int8))
+    _need(k_scale, "k_scale", _BYTE_DTYPES)
+    _need_contiguous(k_scale, "k_scale")
+    _need(cu_seqlens_q, "cu_seqlens_q", _I32, 1)
+    _need_contiguous(cu_seqlens_q, "cu_seqlens_q")
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 0:
+        raise ValueError("cu_seqlens_q needs batch + 1 entries")
+    paged = page_table is not None
+    if paged:
+        if k_fp4.dim() != 4 or tuple(k_fp4.shape[2:]) != (128, 64):
+            raise ValueError("paged k_fp4 must be [num_pages, num_kv_heads, 128, 64]; got %s"
+                             % (tuple(k_fp4.shape),))
+        if not k_fp4[0].is_contiguous():
+            raise ValueError("k_fp4: page contents must be contiguous")
+        num_pages, hkv = k_fp4.shape[:2]
+        page_stride = k_fp4.stride(0)
+        _need_numel(k_scale, "k_scale", num_pages * hkv * 128 * 8)
+        _need(page_table, "page_table", _I32, 2)
+        if page_table.shape[0] < B:
+            raise ValueError("page_table has %d rows; batch is %d" % (page_table.shape[0], B))
+        pt_stride, pt_width = _rows_of(page_table)
+        if seqused_k is None:
+            raise ValueError("paged keys need seqused_k")
+        _need(seqused_k, "seqused_k", _I32, 1)
+        _need_numel(seqused_k, "seqused_k", B)
+        _need_contiguous(seqused_k, "seqused_k")
+        total_k = 0
+        if max_k_tiles is None:
+            max_k_tiles = pt_width
+    else:
+        if k_fp4.dim() != 3 or k_fp4.shape[2] != 64:
+            raise ValueError("flat k_fp4 must be [total_k, num_kv_heads, 64]; got %s"
+                             % (tuple(k_fp4.shape),))
+        _need_contiguous(k_fp4, "k_fp4")
+        total_k, hkv = k_fp4.shape[:2]
+        _need_numel(k_scale, "k_scale", total_k * hkv * 8)
+        if cu_seqlens_k is None:
+            raise ValueError("flat keys need cu_seqlens_k")
+        _need(cu_seqlens_k, "cu_seqlens_k", _I32, 1)
+        _need_numel(cu_seqlens_k, "cu_seqlens_k", B + 1)
+        _need_contiguous(cu_seqlens_k, "cu_seqlens_k")
+        num_pages = page_stride = pt_stride = pt_width = 0
+        if max_k_tiles is None:
+            max_k_tiles = (total_k + 127) // 128
+    if hq % hkv != 0:
+        raise ValueError("num_qo_heads (%d) must be a multiple of num_kv_heads (%d)" % (hq, hkv))
+    dev = _need_device([("q_fp4", q_fp4), ("k_fp4", k_fp4), ("q_scale", q_scale),
+                        ("k_scale", k_scale), ("cu_seqlens_q", cu_seqlens_q),
+                        ("cu_seqlens_k", cu_seqlens_k if not paged else None),
+                        ("page_table", page_table), ("seqused_k", seqused_k if paged else None),
+                        ("output", output),
+                        ("q_offset", q_offset if isinstance(q_offset, torch.Tensor) else None)])
+    if q_offset is not None and not isinstance(q_offset, torch.Tensor):
+        q_offset = torch.full((max(B, 1),), int(q_offset), dtype=torch.int32, device=dev)
+    if q_offset is not None:
+        _need(q_offset, "q_offset", _I32, 1)
+        _need_numel(q_offset, "q_offset", B)
+        _need_contiguous(q_offset, "q_offset")
+    hout = 1 if reduce_heads else hq
+    if output is None:
+        output = torch.empty((hout, max_k_tiles, total_q), dtype=torch.float32, device=dev)
+    _need(output, "output", (torch.float32,), 3)
+    _need_contiguous(output, "output")
+    if tuple(output.shape) != (hout, max_k_tiles, total_q):
+        raise ValueError("output has shape %s; expected %s" % (tuple(output.shape),
+                                                                (hout, max_k_tiles, total_q)))
+    args = (_ptr(q_fp4), _ptr(q_scale), total_q, hq, _ptr(k_fp4), _ptr(k_scale), hkv,
+            page_stride, num_pages, total_k, float(q_global_scale), float(k_global_scale),
+            _ptr(cu_seqlens_q), None if paged else _ptr(cu_seqlens_k),
+            _ptr(page_table), pt_stride, pt_width, _ptr(seqused_k) if paged else None, B,
+            int(bool(causal)), _ptr(q_offset), int(max_seqlen_q or 0), int(max_k_tiles),
+            int(bool(reduce_heads)), _ptr(output), _stream(stream, dev))
+    return output, args, (q_fp4, k_fp4, q_scale, k_scale, cu_seqlens_q, cu_seqlens_k,
+                          page_table, seqused_k, q_offset)
+
+
+def msa_proxy_score_fp4(q_fp4, k_fp4, q_scale, k_scale, q_global_scale, k_global_scale,
+                        cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,
+                        causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
+                        reduce_heads=False, q_offset=None, stream=None):
+    """Per-KV-block max of the causally masked Q K^T logits with NVFP4 inputs.
+
+    q_fp4 uint8 [total_q, Hq, 64] packed e2m1; q_scale e4m3 [total_q*Hq, 8];
+    keys paged (k_fp4 [num_pages, Hkv, 128, 64], k_scale rows
+    (page*Hkv + kv_head)*128 + token, with page_table [batch, width] and
+    seqused_k [batch]) or flat (k_fp4 [total_k, Hkv, 64], k_scale rows
+    token*Hkv + kv_head, with cu_seqlens_k [batch+1]).  q_offset: None (Lk -
+    Lq per request), an int, or an int32 tensor [batch].  Returns float32
+    [Hq or 1, max_k_tiles, total_q]; max_k_tiles defaults to the page-table
+    width (paged) or ceil(total_k / 128) (flat)."""
+    output, args, _ = _proxy_args(q_fp4, k_fp4, q_scale, k_scale, q_global_scale,
+                                  k_global_scale, cu_seqlens_q, cu_seqlens_k, page_table,
+                                  seqused_k, causal, max_seqlen_q, max_k_tiles, output,
+                                  reduce_heads, q_offset, stream)
+    _check(_lib.msa_proxy_score_fp4(*args), "msa_proxy_score_fp4")
+    return output
+
+
+def prepare_msa_proxy_score_fp4(q_fp4, k_fp4, q_scale, k_scale, q_global_scale, k_global_scale,
+                                cu_seqlens_q, cu_seqlens_k=None, *, page_table=None,
+                                seqused_k=None, causal=True, max_seqlen_q=None,
+                                max_k_tiles=None, output=None, reduce_heads=False, q_offset=None,
+                                stream=None):
+    """msa_proxy_score_fp4 with its arguments marshalled once; returns a PreparedCall."""
+    output, args, keep = _proxy_args(q_fp4, k_fp4, q_scale, k_scale, q_global_scale,
+                                     k_global_scale, cu_seqlens_q, cu_seqlens_k, page_table,
+                                     seqused_k, causal, max_seqlen_q, max_k_tiles, output,
+                                     reduce_heads, q_offset, stream)
+    return PreparedCall(_lib.msa_proxy_score_fp4, args, "msa_proxy_score_fp4", output, keep)
 
 
 def prepare_indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpmqa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "mqa_logits.hip", "mqa_any.hip", "indexer.hip"]
+SOURCES = ["api.hip", "mqa_logits.hip", "mqa_any.hip", "indexer.hip", "proxy.hip"]
 ARCH = "gfx950"
 
 
@@ -32,7 +32,8 @@ def hipcc() -> str:
 # of accumulation registers), and no NaN semantics for arithmetic so the
 # rectifier is one v_max_f32 (NaN outputs are written as bit patterns there).
 _LOGITS_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"mqa_logits.hip": _LOGITS_FLAGS, "mqa_any.hip": _LOGITS_FLAGS}
+EXTRA_FLAGS = {"mqa_logits.hip": _LOGITS_FLAGS, "mqa_any.hip": _LOGITS_FLAGS,
+               "proxy.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def compile_flags(src=None):

@@ -1,6 +1,7 @@
 // C ABI of libpmqa.so (declared in include/pmqa.h): host-side validation,
 // per-device cached facts, and kernel launches.  No entry point allocates,
 // synchronises or reads device memory.
+#include <algorithm>
 #include <mutex>
 
 #include "pmqa.h"
@@ -22,7 +23,12 @@ struct DeviceInfo {
   size_t static_lds[kFastSlots][kKernelVariants][2] = {};
   int occ_any[2][2] = {};
   size_t static_lds_any[2][2] = {};
+  // proxy score kernels [row tiles 1, 2, 4 -> 0, 1, 2][reduce]
+  int occ_proxy[3][2] = {};
+  size_t static_lds_proxy[3][2] = {};
 };
+
+int proxy_nt_index(int nt) { return nt == 1 ? 0 : nt == 2 ? 1 : 2; }
 
 // Resident workgroups per CU of a kernel whose register limit is `occ`,
 // launched with `dyn_lds` bytes of dynamic LDS and `static_lds` of static LDS
@@ -88,6 +94,11 @@ int init_device(int device) {
       for (int o = 0; o < 2 && rc == PMQA_OK; ++o)
         if (!query_kernel(mqa_any_kernel_symbol(ks, o), &d.occ_any[ks - 1][o],
                           &d.static_lds_any[ks - 1][o]))
+          rc = PMQA_ERR_HIP;
+    for (int i = 0; i < 3 && rc == PMQA_OK; ++i)
+      for (int red = 0; red < 2 && rc == PMQA_OK; ++red)
+        if (!query_kernel(proxy_kernel_symbol(1 << i, red), &d.occ_proxy[i][red],
+                          &d.static_lds_proxy[i][red]))
           rc = PMQA_ERR_HIP;
     hipFuncAttributes attr;
     if (rc == PMQA_OK && (hipFuncGetAttributes(&attr, schedule_kernel_symbol()) != hipSuccess ||
@@ -370,6 +381,89 @@ int indexer_scores_nvfp4(const void* query, const void* query_scales, int32_t ro
   a.uniform_g = uniform_g;
   a.max_context = max_context;
   if (launch_indexer_nvfp4(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PMQA_ERR_HIP;
+  return PMQA_OK;
+}
+
+int msa_proxy_score_fp4(const void* q_fp4, const void* q_scale, int32_t total_q,
+                        int32_t num_qo_heads, const void* k_fp4, const void* k_scale,
+                        int32_t num_kv_heads, int64_t page_stride, int32_t num_pages,
+                        int64_t total_k, float q_global_scale, float k_global_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* page_table, int64_t pt_stride, int32_t pt_width,
+                        const int32_t* seqused_k, int32_t batch, int32_t causal,
+                        const int32_t* q_offset, int32_t max_seqlen_q, int32_t max_k_tiles,
+                        int32_t reduce_heads, float* out, void* stream) {
+  const bool paged = page_table != nullptr;
+  if (total_q < 0 || batch < 0 || max_k_tiles < 0 || max_seqlen_q < 0) return PMQA_ERR_SHAPE;
+  if (num_qo_heads < 1 || num_kv_heads < 1 || num_qo_heads % num_kv_heads != 0)
+    return PMQA_ERR_SHAPE;
+  const int group = num_qo_heads / num_kv_heads;
+  if (group > 64 || batch > kProxyMaxBatch) return PMQA_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_heads * total_q * max_k_tiles >= ((int64_t)1 << 31))
+    return PMQA_ERR_UNSUPPORTED;
+  if (total_q == 0 || max_k_tiles == 0) return PMQA_OK;  // no output
+  if (!out || !cu_seqlens_q) return PMQA_ERR_NULL;
+  if (batch > 0) {
+    if (!q_fp4 || !q_scale || !k_fp4 || !k_scale) return PMQA_ERR_NULL;
+    if (paged) {
+      if (!seqused_k) return PMQA_ERR_NULL;
+      if (num_pages < 1 || pt_width < 1 || pt_stride < pt_width) return PMQA_ERR_SHAPE;
+      if (pt_width > (1 << 23)) return PMQA_ERR_UNSUPPORTED;
+      if (page_stride < (int64_t)num_kv_heads * 128 * 64) return PMQA_ERR_SHAPE;
+      if (page_stride % 16 != 0) return PMQA_ERR_ALIGN;
+    } else {
+      if (!cu_seqlens_k) return PMQA_ERR_NULL;
+      if (total_k < 0) return PMQA_ERR_SHAPE;
+    }
+  }
+  if (((uintptr_t)q_fp4 | (uintptr_t)k_fp4) & 15) return PMQA_ERR_ALIGN;
+  if (((uintptr_t)q_scale | (uintptr_t)k_scale) & 1) return PMQA_ERR_ALIGN;
+  if (((uintptr_t)out | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k |
+       (uintptr_t)page_table | (uintptr_t)seqused_k | (uintptr_t)q_offset) & 3)
+    return PMQA_ERR_ALIGN;
+  DeviceInfo* d = nullptr;
+  int rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
+  // row tiles: every query head of a KV head's group for as many tokens as
+  // the longest request has, up to 64 rows
+  const int maxq = max_seqlen_q > 0 ? max_seqlen_q : (total_q > 0 ? total_q : 1);
+  const int64_t want = std::min<int64_t>((int64_t)group * maxq, 64);
+  const int nt = want <= 16 ? 1 : want <= 32 ? 2 : 4;
+  int tc = 16 * nt / group;
+  if (tc > maxq) tc = maxq;
+  if (tc < 1) tc = 1;
+  ProxyArgs a;
+  a.q = static_cast<const uint8_t*>(q_fp4);
+  a.qs = static_cast<const uint8_t*>(q_scale);
+  a.k = static_cast<const uint8_t*>(k_fp4);
+  a.ks = static_cast<const uint8_t*>(k_scale);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = paged ? nullptr : cu_seqlens_k;
+  a.pt = paged ? page_table : nullptr;
+  a.seqused = paged ? seqused_k : nullptr;
+  a.q_offset = q_offset;
+  a.out = out;
+  a.page_stride = paged ? page_stride : 0;
+  a.pt_stride = paged ? pt_stride : 0;
+  a.total_k = paged ? 0 : total_k;
+  a.pt_width = paged ? pt_width : 0;
+  a.num_pages = paged ? num_pages : 0;
+  a.total_q = total_q;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.group = group;
+  a.tc = tc;
+  a.batch = batch;
+  a.max_k_tiles = max_k_tiles;
+  a.causal = causal ? 1 : 0;
+  a.paged = paged ? 1 : 0;
+  a.reduce = reduce_heads ? 1 : 0;
+  a.g = q_global_scale * k_global_scale;
+  const int i = proxy_nt_index(nt);
+  const int per_cu = limit_by_lds(*d, d->occ_proxy[i][a.reduce], d->static_lds_proxy[i][a.reduce],
+                                  proxy_lds_bytes(batch));
+  if (launch_proxy(a, nt, d->cus * per_cu, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PMQA_ERR_HIP;
   return PMQA_OK;
 }

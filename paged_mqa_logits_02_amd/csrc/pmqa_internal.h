@@ -58,6 +58,36 @@ struct IdxArgs {
   int max_context;
 };
 
+// Arguments of the block-max proxy score kernel (NVFP4 query and keys).
+struct ProxyArgs {
+  const uint8_t* q;         // packed e2m1 [total_q, hq, 64]
+  const uint8_t* qs;        // e4m3 [total_q * hq, 8]
+  const uint8_t* k;         // paged: page i at k + i*page_stride, [hkv, 128, 64]; flat: [total_k, hkv, 64]
+  const uint8_t* ks;        // e4m3 rows of 8: paged (page*hkv + kv_head)*128 + token; flat token*hkv + kv_head
+  const int32_t* cu_q;      // [batch+1]
+  const int32_t* cu_k;      // flat: [batch+1]
+  const int32_t* pt;        // paged: [batch, pt_stride]
+  const int32_t* seqused;   // paged: [batch]
+  const int32_t* q_offset;  // [batch] or null (Lk - Lq)
+  float* out;               // [reduce ? 1 : hq, max_k_tiles, total_q]
+  long long page_stride;
+  long long pt_stride;
+  long long total_k;        // flat: key rows per KV head
+  int pt_width;
+  int num_pages;
+  int total_q;
+  int hq, hkv, group;       // group = hq / hkv
+  int tc;                   // query tokens per unit
+  int batch;
+  int max_k_tiles;
+  int causal, paged, reduce;
+  float g;                  // q_global_scale * k_global_scale
+};
+constexpr int kProxyMaxBatch = 4096;  // request tables kept in LDS
+const void* proxy_kernel_symbol(int nt, int reduce);
+size_t proxy_lds_bytes(int batch);
+hipError_t launch_proxy(const ProxyArgs& a, int nt, int grid, hipStream_t stream);
+
 // Kernels for 64 heads and head_dim 128, one instance per slot count of a
 // pass (1..kFastSlots) and kernel variant: 0 is FP8; 1..4 are MXFP4 with
 // one e8m0 code per sf_vec_size values (32 or 16), the key codes either

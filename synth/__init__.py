@@ -506,7 +506,8 @@ def make_proxy_inputs(q_lens, k_lens, *, num_qo_heads=64, num_kv_heads=8, paged=
 
 SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5,
          "indexer_nvfp4": 6, "verify_fp8_n8": 7, "verify_fp8_h32": 8, "verify_fp8_bf16": 4,
-         "mxfp4_n4": 9, "mxfp4_sf16": 5, "mxfp4_records": 5, "mxfp4_sf16_records": 5}
+         "mxfp4_n4": 9, "mxfp4_sf16": 5, "mxfp4_records": 5, "mxfp4_sf16_records": 5,
+         "proxy_decode": 10, "proxy_verify": 11}
 
 # the MXFP4 scale layouts of the mxfp4 workload: (sf_vec_size, interleaved)
 MX_LAYOUT_CONFIGS = {"mxfp4": (32, False), "mxfp4_sf16": (16, False),
@@ -521,7 +522,7 @@ def _lens(name, rng):
         return rng.integers(4096, 65536 + 1, size=128).astype(np.int32)
     if name == "verify_fp8_n8":
         return rng.integers(4096, 65536 + 1, size=64).astype(np.int32)
-    if name in ("mxfp4_n4",) or name in MX_LAYOUT_CONFIGS:
+    if name in ("mxfp4_n4", "proxy_decode", "proxy_verify") or name in MX_LAYOUT_CONFIGS:
         return rng.integers(16384, 131072 + 1, size=64).astype(np.int32)
     raise KeyError(name)
 
@@ -546,6 +547,10 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
     mxfp4_sf16, mxfp4_records, mxfp4_sf16_records
                  mxfp4 (same seed and lengths) with one code per 16 values,
                  with each token's codes after its packed bytes, or both
+    proxy_decode block-max proxy score: B=64 requests of 1 query token, 64
+                 query heads over 8 KV heads (head_dim 128), paged NVFP4 keys,
+                 key counts uniform in 16K..128K, causal, 1024 blocks per row
+    proxy_verify the same with 4 query tokens per request
     """
     if seed is None:
         seed = SEEDS[name]
@@ -556,6 +561,13 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
         kw = dict(fmt="bf16" if name == "indexer_bf16" else "nvfp4")
         kw.update(overrides)
         return make_indexer_inputs(seed=seed, name=name, **kw)
+    elif name in ("proxy_decode", "proxy_verify"):
+        lens = _lens(name, np.random.default_rng(seed + 1000))
+        lq = 1 if name == "proxy_decode" else 4
+        kw = dict(q_lens=[lq] * len(lens), k_lens=lens, num_qo_heads=64, num_kv_heads=8,
+                  paged=True, causal=True, max_k_tiles=1024, pt_width=1024, quantize=False)
+        kw.update(overrides)
+        return make_proxy_inputs(seed=seed, name=name, **kw)
     elif name in ("decode_fp8", "verify_fp8", "verify_fp8_n8", "verify_fp8_h32",
                   "verify_fp8_bf16", "mxfp4_n4") or name in MX_LAYOUT_CONFIGS:
         lens = _lens(name, np.random.default_rng(seed + 1000))
