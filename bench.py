@@ -63,6 +63,10 @@ WORKLOADS = {
                     "context lengths uniform 0..4096 (one 0), fp32 scores",
     "indexer_nvfp4": "as indexer_bf16 with NVFP4 query and keys (packed e2m1, e4m3 scale per "
                      "16 values, key scales paged like the keys)",
+    "indexer_bf16_8k": "8192 query rows in groups of 1..8 over 512 requests, d=128, bf16 key "
+                       "pages of 64 (64 per request), context lengths uniform 0..4096, fp32 "
+                       "scores [8192, 4096]",
+    "indexer_nvfp4_8k": "indexer_bf16_8k with NVFP4 query and keys",
 }
 
 
@@ -188,9 +192,29 @@ def copy_calibration(steps):
                       "gb_per_s": 2 * n / dt / 1e9}))
 
 
+def gemm_calibration(steps):
+    """A compute-bound library kernel (bf16 GEMM 8192^3 on the matrix cores),
+    for reading the engine clock under matrix load from the profiler's
+    cycle counters."""
+    import torch
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        c = a @ b
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"gemm_n": n, "ms": dt * 1e3, "tflops": 2 * n ** 3 / dt / 1e12,
+                      "check": float(c[0, 0])}))
+
+
 def run_indexer(args, torch, synth, pm, dev):
     """The one-head indexer workloads: one indexer_scores call per step."""
-    nvfp4 = args.workload == "indexer_nvfp4"
+    nvfp4 = args.workload.startswith("indexer_nvfp4")
     inp = synth.make_config(args.workload)
     key_bytes = inp.key_cache.nbytes + (inp.key_scales.nbytes if nvfp4 else 0)
     R = args.replicas or max(2, -(-2 * MALL_BYTES // key_bytes))
@@ -363,7 +387,11 @@ def main():
     ap.add_argument("--launch-events", action="store_true",
                     help="also time every launch with its own pair of events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workspace", action="store_true",
+                    help="give the logits calls a workspace: a work counter with which the "
+                         "workgroups that finish first take the call's last items in chunks")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--gemm-calibration", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -375,6 +403,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.gemm_calibration:
+        gemm_calibration(args.steps)
         return
 
     import synth
@@ -407,6 +438,8 @@ def main():
     U = pm.num_units(inp.next_n, variant)
     sched = torch.empty(pm.schedule_ints(U), dtype=torch.int32, device=dev)
     mx_layout = dict(sf_vec_size=inp.sf_vec_size, is_kv_sf_interleaved=inp.kv_sf_interleaved)
+    # the work counter of the in-call split (caller workspace), if asked for
+    ws = pm.workspace(dev) if args.workspace else None
     stream = torch.cuda.current_stream(dev)
 
     def step(i, st, ev0=None, ev1=None):
@@ -419,10 +452,11 @@ def main():
             ev0.record(st)
         if variant == 0:
             pm.mqa_logits_fp8(q, kv[i % R], w, sl, bt, max_context=inp.max_context,
-                              out=outs[i % 2], schedule_meta=s, stream=st)
+                              out=outs[i % 2], schedule_meta=s, stream=st, workspace=ws)
         else:
             pm.mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt, max_context=inp.max_context,
-                                out=outs[i % 2], schedule_meta=s, stream=st, **mx_layout)
+                                out=outs[i % 2], schedule_meta=s, stream=st, workspace=ws,
+                                **mx_layout)
         if ev1 is not None:
             ev1.record(st)
 
@@ -442,12 +476,13 @@ def main():
         if variant == 0:
             calls.append(pm.prepare_mqa_logits_fp8(q, kv[i % R], w, sl, bt,
                                                    max_context=inp.max_context, out=outs[i % 2],
-                                                   schedule_meta=s_meta, stream=stream))
+                                                   schedule_meta=s_meta, stream=stream,
+                                                   workspace=ws))
         else:
             calls.append(pm.prepare_mqa_logits_mxfp4(q, q_sf, kv[i % R], w, sl, bt,
                                                      max_context=inp.max_context,
                                                      out=outs[i % 2], schedule_meta=s_meta,
-                                                     stream=stream, **mx_layout))
+                                                     stream=stream, workspace=ws, **mx_layout))
 
     def fast_step(i, ev0=None, ev1=None):
         if args.mode == "schedule":
@@ -556,6 +591,7 @@ def main():
             "head_dim": inp.head_dim, "max_context": inp.max_context,
             "kv_positions": positions, "pages": int(inp.num_pages),
             "schedule": args.mode, "kv_replicas": R, "units": U,
+            "work_counter": bool(args.workspace and args.mode == "in_call"),
             "products": ("f16 MFMA of exactly widened e4m3, fp32 sums" if inp.variant == "fp8"
                          else "scaled e2m1 MFMA, fp32 sums"),
             **({} if inp.variant == "fp8" else {

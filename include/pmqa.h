@@ -50,6 +50,7 @@ typedef enum {
     PMQA_ERR_SHAPE = -2,       /* a size or stride is out of range              */
     PMQA_ERR_UNSUPPORTED = -3, /* a valid but unimplemented option              */
     PMQA_ERR_ALIGN = -4,       /* a pointer or stride is not aligned as needed  */
+    PMQA_ERR_WORKSPACE = -5,   /* workspace smaller than mqa_logits_workspace_bytes() */
     PMQA_ERR_HIP = -6          /* the HIP runtime reported an error             */
 } pmqa_status;
 
@@ -99,6 +100,19 @@ enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_MXFP4 = 1 };
  *                ("flashinfer.attn_scores", Scheduling and Setup, and its warning).
  *                A schedule built for other arguments is detected on the device
  *                and ignored.
+ *   workspace, workspace_bytes
+ *                NULL, or caller-owned device memory of at least
+ *                mqa_logits_workspace_bytes() bytes, 16-B aligned (smaller ->
+ *                PMQA_ERR_WORKSPACE), zero-filled before its first use.  Used
+ *                only when schedule is NULL, by the 64-head x 128 kernels: it
+ *                holds a work counter with which the workgroups that finish
+ *                their share first take the last items of the call in small
+ *                chunks (the per-call work assignment on the GPU of
+ *                "flashinfer.attn_scores", Scheduling and Setup).  Every
+ *                completed call leaves it zero-filled again, so calls and graph
+ *                replays need no clearing; two calls that may run at the same
+ *                time must not share one.  NULL: the kernel's static split.
+ *                The logits do not depend on the split.
  *   Supported (the FP8 variant's shapes are parametric: "flashinfer.attn_scores",
  *   paragraph on how the variants differ): 1 <= num_heads <= 128,
  *   head_dim a multiple of 16 in 16..256, 1 <= next_n <= 8; other values ->
@@ -112,7 +126,8 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
                    int64_t bt_stride, int32_t bt_width, int32_t batch, int32_t next_n,
                    int32_t num_heads, int32_t head_dim, void* out, int64_t out_row_stride,
                    int32_t max_context, int32_t out_dtype, int32_t acc_dtype,
-                   const int32_t* schedule, void* stream);
+                   const int32_t* schedule, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * mqa_logits_mxfp4 - MXFP4 paged MQA logits (no s_p; block scales folded).
@@ -153,7 +168,8 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
                      const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
                      int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
                      void* out, int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
-                     const int32_t* schedule, void* stream);
+                     const int32_t* schedule, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * indexer_scores - one-head BF16 indexer scores.
@@ -295,6 +311,13 @@ int mqa_logits_schedule(const int32_t* seq_lens, int32_t batch, int32_t next_n, 
 
 /* Number of int32 entries of a schedule buffer for num_units units. */
 int64_t mqa_logits_schedule_ints(int32_t num_units);
+
+/*
+ * mqa_logits_workspace_bytes - bytes of the optional workspace of
+ * mqa_logits_fp8 / mqa_logits_mxfp4 (a work counter; the same for every call
+ * and device).  See the workspace argument of mqa_logits_fp8.
+ */
+size_t mqa_logits_workspace_bytes(void);
 
 /* The unit count a NULL-schedule call with 64 heads and head_dim 128 uses on
  * `device` for this next_n and variant: the workgroups of the call's first

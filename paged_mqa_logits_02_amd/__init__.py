@@ -47,10 +47,13 @@ def _load():
                           "python paged_mqa_logits_02_amd/build.py" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    SZ = ctypes.c_size_t
     lib.mqa_logits_fp8.argtypes = [P, P, I64, I32, P, P, P, I64, I32, I32, I32, I32, I32, P, I64,
-                                   I32, I32, I32, P, P]
+                                   I32, I32, I32, P, P, SZ, P]
     lib.mqa_logits_mxfp4.argtypes = [P, P, I32, I32, P, I64, I32, P, P, P, I64, I32, I32, I32,
-                                     I32, I32, P, I64, I32, I32, P, P]
+                                     I32, I32, P, I64, I32, I32, P, P, SZ, P]
+    lib.mqa_logits_workspace_bytes.argtypes = []
+    lib.mqa_logits_workspace_bytes.restype = SZ
     lib.indexer_scores.argtypes = [P, I32, I32, P, I64, I32, P, I64, I32, I32, P, P, I32, P, P,
                                    I64, I32, P]
     lib.indexer_scores_nvfp4.argtypes = [P, P, I32, I32, P, I64, P, I64, I32, P, I64, I32, I32,
@@ -320,8 +323,37 @@ def _check_mqa(q, q_sf, kv_fused, weights, seq_lens, block_table, out, schedule_
                          ("schedule_meta", schedule_meta)])
 
 
+def _workspace_args(workspace, device):
+    """(pointer, bytes) of an optional workspace tensor (see workspace())."""
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor):
+        raise ValueError("workspace must be a torch.Tensor")
+    _need_contiguous(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < workspace_bytes():
+        raise ValueError("workspace holds %d bytes; %d are needed" % (nbytes, workspace_bytes()))
+    if not workspace.is_cuda or workspace.device != device:
+        raise ValueError("workspace is on %s; the other tensors on %s" % (workspace.device, device))
+    return _ptr(workspace), nbytes
+
+
+def workspace_bytes() -> int:
+    """Bytes of the optional work-counter workspace of the logits calls."""
+    return int(_lib.mqa_logits_workspace_bytes())
+
+
+def workspace(device=None) -> torch.Tensor:
+    """A zero-filled workspace for mqa_logits_fp8 / mqa_logits_mxfp4 (workspace=):
+    every completed call leaves it zero-filled, so one allocation serves any
+    number of calls that do not run at the same time."""
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
+
+
 def _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
-              schedule_meta, output_dtype, acc_dtype, stream):
+              schedule_meta, output_dtype, acc_dtype, stream, workspace=None):
     _need(q, "q", _BYTE_DTYPES, 4)
     B, N, H, D = q.shape
     if next_n is not None and next_n != N:
@@ -336,14 +368,17 @@ def _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, 
     ors, _ = _rows_of(out)
     ps, npages = _pages(kv_fused)
     acc = _dtype_code(acc_dtype) if acc_dtype in (torch.float32, torch.bfloat16) else 99
+    wp, wb = _workspace_args(workspace, q.device)
     return out, (_ptr(q), _ptr(kv_fused), ps, npages, _ptr(weights), _ptr(seq_lens),
                  _ptr(block_table), bt_stride, bt_width, B, N, H, D, _ptr(out), ors, max_context,
-                 _dtype_code(out.dtype), acc, _ptr(schedule_meta), _stream(stream, q.device))
+                 _dtype_code(out.dtype), acc, _ptr(schedule_meta), wp, wb,
+                 _stream(stream, q.device))
 
 
 def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                    max_context=None, out=None, schedule_meta=None,
-                   output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
+                   output_dtype=torch.float32, acc_dtype=torch.float32, stream=None,
+                   workspace=None):
     """FP8 paged MQA logits; returns ``out`` [batch*next_n, max_context].
 
     q [batch, next_n, heads, head_dim] e4m3 (uint8 or float8_e4m3fn; heads
@@ -352,15 +387,17 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
     [batch*next_n, heads] fp32; seq_lens [batch] int32; block_table
     [batch, width] int32.  Columns at or beyond ceil(seq_len/64)*64 and rows
     of empty requests are not written (out=None allocates uninitialised
-    memory)."""
+    memory).  workspace: None or workspace(), a work counter for the in-call
+    split (the result does not depend on it)."""
     out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
-                          schedule_meta, output_dtype, acc_dtype, stream)
+                          schedule_meta, output_dtype, acc_dtype, stream, workspace)
     _check(_lib.mqa_logits_fp8(*args), "mqa_logits_fp8")
     return out
 
 
 def _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n, sf_vec_size,
-                is_kv_sf_interleaved, max_context, out, schedule_meta, output_dtype, stream):
+                is_kv_sf_interleaved, max_context, out, schedule_meta, output_dtype, stream,
+                workspace=None):
     _need(q, "q", (torch.uint8, torch.int8), 4)
     B, N, H, Dh = q.shape
     if next_n is not None and next_n != N:
@@ -383,15 +420,17 @@ def _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n, sf_ve
     _need_rows(out, "out", B * N, max_context)
     ors, _ = _rows_of(out)
     ps, npages = _pages(kv_fused)
+    wp, wb = _workspace_args(workspace, q.device)
     return out, (_ptr(q), _ptr(q_sf), sf_vec_size, int(is_kv_sf_interleaved), _ptr(kv_fused), ps,
                  npages, _ptr(weights), _ptr(seq_lens), _ptr(block_table), bt_stride, bt_width,
                  B, N, H, Dh * 2, _ptr(out), ors, max_context, _dtype_code(out.dtype),
-                 _ptr(schedule_meta), _stream(stream, q.device))
+                 _ptr(schedule_meta), wp, wb, _stream(stream, q.device))
 
 
 def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                      sf_vec_size=32, is_kv_sf_interleaved=False, max_context=None, out=None,
-                     schedule_meta=None, output_dtype=torch.bfloat16, stream=None):
+                     schedule_meta=None, output_dtype=torch.bfloat16, stream=None,
+                     workspace=None):
     """MXFP4 paged MQA logits; returns ``out`` [batch*next_n, max_context].
 
     q [batch, next_n, 64, 64] packed e2m1 uint8; q_sf [batch, next_n, 64,
@@ -402,7 +441,7 @@ def mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=N
     bytes followed by its codes."""
     out, args = _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n,
                             sf_vec_size, is_kv_sf_interleaved, max_context, out, schedule_meta,
-                            output_dtype, stream)
+                            output_dtype, stream, workspace)
     _check(_lib.mqa_logits_mxfp4(*args), "mqa_logits_mxfp4")
     return out
 
@@ -427,24 +466,26 @@ class PreparedCall:
 
 def prepare_mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                            max_context=None, out=None, schedule_meta=None,
-                           output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
+                           output_dtype=torch.float32, acc_dtype=torch.float32, stream=None,
+                           workspace=None):
     """mqa_logits_fp8 with its arguments marshalled once; returns a PreparedCall."""
     out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
-                          schedule_meta, output_dtype, acc_dtype, stream)
+                          schedule_meta, output_dtype, acc_dtype, stream, workspace)
     return PreparedCall(_lib.mqa_logits_fp8, args, "mqa_logits_fp8", out,
-                        (q, kv_fused, weights, seq_lens, block_table, schedule_meta))
+                        (q, kv_fused, weights, seq_lens, block_table, schedule_meta, workspace))
 
 
 def prepare_mqa_logits_mxfp4(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n=None, *,
                              sf_vec_size=32, is_kv_sf_interleaved=False, max_context=None,
                              out=None, schedule_meta=None, output_dtype=torch.bfloat16,
-                             stream=None):
+                             stream=None, workspace=None):
     """mqa_logits_mxfp4 with its arguments marshalled once; returns a PreparedCall."""
     out, args = _mxfp4_args(q, q_sf, kv_fused, weights, seq_lens, block_table, next_n,
                             sf_vec_size, is_kv_sf_interleaved, max_context, out, schedule_meta,
-                            output_dtype, stream)
+                            output_dtype, stream, workspace)
     return PreparedCall(_lib.mqa_logits_mxfp4, args, "mqa_logits_mxfp4", out,
-                        (q, q_sf, kv_fused, weights, seq_lens, block_table, schedule_meta))
+                        (q, q_sf, kv_fused, weights, seq_lens, block_table, schedule_meta,
+                         workspace))
 
 
 def indexer_scores(query, key_cache, block_table, context_lengths, *, requests, scores,

@@ -154,7 +154,7 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
             int32_t num_pages, const float* w, const int32_t* seq_lens, const int32_t* bt,
             int64_t bt_stride, int32_t batch, int32_t next_n, int32_t heads, int32_t head_dim,
             int variant, void* out, int64_t out_row_stride, int32_t max_context,
-            int32_t out_dtype, const int32_t* schedule, void* stream) {
+            int32_t out_dtype, const int32_t* schedule, WorkCounter* work, void* stream) {
   DeviceInfo* d = nullptr;
   int rc = current_device_info(&d);
   if (rc != PMQA_OK) return rc;
@@ -178,6 +178,8 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
   a.head_dim = head_dim;
   a.cus = d->cus;
   a.split_skew = 0;
+  a.dyn_share = 0;
+  a.dyn_chunk = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t prefix = (size_t)(batch + 1) * sizeof(int);
   if (heads == 64 && head_dim == 128) {
@@ -186,8 +188,13 @@ int run_mqa(const void* q, const void* q_sf, const void* kv, int64_t page_stride
       a.slots = next_n - s0 < kFastSlots ? next_n - s0 : kFastSlots;
       const size_t lds = mqa_ring_bytes(variant, a.slots) + prefix;
       a.split_skew = split_skew_for(a.slots, variant);
+      a.dyn_share = dyn_share_for(a.slots, variant);
+      a.dyn_chunk = dyn_chunk_for(a.slots, variant);
       const int grid = d->cus * blocks_per_cu(*d, a.slots, variant, out_dtype, lds);
-      if (launch_mqa(a, a.slots, variant, out_dtype, grid, lds, s) != hipSuccess)
+      // the counter serves the in-call split only; the launches of one call
+      // run one after the other on the stream, each leaving it zero
+      if (launch_mqa(a, a.slots, variant, out_dtype, grid, lds, schedule ? nullptr : work, s) !=
+          hipSuccess)
         return PMQA_ERR_HIP;
     }
     return PMQA_OK;
@@ -214,12 +221,24 @@ using namespace pmqa;
 
 extern "C" {
 
+// A caller workspace: NULL (no work counter), or at least kWorkspaceBytes,
+// 16-B aligned.
+static int check_workspace(const void* workspace, size_t workspace_bytes) {
+  if (!workspace) return PMQA_OK;
+  if (workspace_bytes < kWorkspaceBytes) return PMQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PMQA_ERR_ALIGN;
+  return PMQA_OK;
+}
+
 int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int32_t num_pages,
                    const float* weights, const int32_t* seq_lens, const int32_t* block_table,
                    int64_t bt_stride, int32_t bt_width, int32_t batch, int32_t next_n,
                    int32_t num_heads, int32_t head_dim, void* out, int64_t out_row_stride,
                    int32_t max_context, int32_t out_dtype, int32_t acc_dtype,
-                   const int32_t* schedule, void* stream) {
+                   const int32_t* schedule, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int wrc = check_workspace(workspace, workspace_bytes);
+  if (wrc != PMQA_OK) return wrc;
   if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
   if (num_heads > kAnyMaxHeads || head_dim > kAnyMaxDim || head_dim % 16 != 0)
     return PMQA_ERR_UNSUPPORTED;
@@ -231,7 +250,8 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
   if (rc != PMQA_OK || batch == 0 || max_context == 0) return rc;
   return run_mqa(q, nullptr, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
                  bt_stride, batch, next_n, num_heads, head_dim, PMQA_VARIANT_FP8, out,
-                 out_row_stride, max_context, out_dtype, schedule, stream);
+                 out_row_stride, max_context, out_dtype, schedule,
+                 static_cast<WorkCounter*>(workspace), stream);
 }
 
 int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
@@ -240,7 +260,10 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
                      const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
                      int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
                      void* out, int64_t out_row_stride, int32_t max_context, int32_t out_dtype,
-                     const int32_t* schedule, void* stream) {
+                     const int32_t* schedule, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int wrc = check_workspace(workspace, workspace_bytes);
+  if (wrc != PMQA_OK) return wrc;
   if (num_heads < 1 || head_dim < 1) return PMQA_ERR_SHAPE;
   if (num_heads != 64 || head_dim != 128) return PMQA_ERR_UNSUPPORTED;
   if (sf_vec_size != 16 && sf_vec_size != 32) return PMQA_ERR_UNSUPPORTED;
@@ -254,7 +277,7 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
   return run_mqa(q, q_sf, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
                  bt_stride, batch, next_n, num_heads, head_dim,
                  mx_kernel_variant(sf_vec_size, is_kv_sf_interleaved), out, out_row_stride,
-                 max_context, out_dtype, schedule, stream);
+                 max_context, out_dtype, schedule, static_cast<WorkCounter*>(workspace), stream);
 }
 
 // Validation shared by both indexer entry points; key_bytes is the packed size
@@ -468,6 +491,8 @@ int msa_proxy_score_fp4(const void* q_fp4, const void* q_scale, int32_t total_q,
   return PMQA_OK;
 }
 
+size_t mqa_logits_workspace_bytes(void) { return kWorkspaceBytes; }
+
 int64_t mqa_logits_schedule_ints(int32_t num_units) {
   if (num_units < 1 || num_units > (1 << 20)) return -1;
   return kSchedHeader + 3 * ((int64_t)num_units + 1);
@@ -542,6 +567,7 @@ const char* mqa_logits_status_string(int status) {
     case PMQA_ERR_SHAPE: return "PMQA_ERR_SHAPE: a size or stride is out of range";
     case PMQA_ERR_UNSUPPORTED: return "PMQA_ERR_UNSUPPORTED: option not implemented";
     case PMQA_ERR_ALIGN: return "PMQA_ERR_ALIGN: pointer or stride misaligned";
+    case PMQA_ERR_WORKSPACE: return "PMQA_ERR_WORKSPACE: workspace smaller than mqa_logits_workspace_bytes()";
     case PMQA_ERR_HIP: return "PMQA_ERR_HIP: the HIP runtime reported an error";
     default: return "unknown pmqa status";
   }

@@ -816,13 +816,33 @@ constexpr int ring_bytes() {
 // The tensor pointers are separate __restrict__ parameters so the compiler
 // knows the kernel's stores never alias its inputs and keeps wave-uniform
 // reads (block table, seq_lens, schedule) on the scalar cache.
+// The next chunk of the workgroup's pool for the whole workgroup: one lane
+// takes it from the pool's counter with a vector-memory atomic (never a
+// scalar one) and shares it through LDS.  No load into LDS is in flight here
+// (every range ends with its loads waited for), so a plain barrier is safe.
+// A pool of NC chunks shared by W workgroups sees exactly NC + W grabs (each
+// workgroup grabs until it draws past the pool), so the grab that draws
+// NC + W - 1 is the pool's last: it returns the counter to zero, and the next
+// launch (or graph replay) needs no clearing.
+__device__ __forceinline__ int grab_chunk(WorkCounter* ctr, int last_grab, int* s_slot) {
+  if (threadIdx.x == 0) {
+    const int c = __hip_atomic_fetch_add(&ctr->next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c == last_grab) __hip_atomic_store(&ctr->next, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_slot = c;
+  }
+  __syncthreads();
+  const int c = uniform(*s_slot);
+  __syncthreads();  // every wave has read the slot before it is written again
+  return c;
+}
+
 template <int N, int VAR, int OUTT>
 __global__ void __launch_bounds__(256)
     mqa_logits_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sf,
                       const uint8_t* __restrict__ kv, const float* __restrict__ w,
                       const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bt,
                       const int32_t* __restrict__ schedule, void* __restrict__ out,
-                      const MqaArgs dims) {
+                      WorkCounter* __restrict__ work, const MqaArgs dims) {
   MqaArgs a = dims;
   a.q = q;
   a.q_sf = q_sf;
@@ -865,10 +885,34 @@ __global__ void __launch_bounds__(256)
       ring_barrier();  // the ring and the page-id table are reused by the next unit
     }
   } else {
+    // Equal (round-weighted) static ranges over the first S items; with a
+    // work counter, the last P - S items are dealt in chunks to whichever
+    // workgroups finish their range first, from one pool per XCD (a
+    // contiguous share of the dynamic items, and its own counter, so that
+    // the grabs of the 8 XCDs do not queue on one address).
     const long long P = uniform(s_prefix[a.batch]);
-    const long long f0 = split_point(unit, G, a.cus, a.split_skew, P);
-    const long long f1 = split_point(unit + 1, G, a.cus, a.split_skew, P);
-    if (f1 > f0) process_range<N, VAR, OUTT>(a, s_prefix, s_pid, ring, f0, (int)(f1 - f0));
+    long long S = P, C = 1, D = 0;
+    if (work != nullptr) {
+      C = a.dyn_chunk > 0 ? a.dyn_chunk : 1;
+      D = P * a.dyn_share / 1024;
+      S = P - D;
+    }
+    long long f0 = split_point(unit, G, a.cus, a.split_skew, S);
+    long long cnt = split_point(unit + 1, G, a.cus, a.split_skew, S) - f0;
+    const int pools = (G % kXcds == 0) ? kXcds : 1;
+    const int pool = pools == kXcds ? blockIdx.x % kXcds : 0;
+    const long long p0 = S + D * pool / pools, p1 = S + D * (pool + 1) / pools;
+    const int NC = (int)((p1 - p0 + C - 1) / C);
+    const int last_grab = NC + G / pools - 1;
+    while (true) {
+      if (cnt > 0) process_range<N, VAR, OUTT>(a, s_prefix, s_pid, ring, f0, (int)cnt);
+      if (work == nullptr) break;
+      ring_barrier();  // the ring and the page-id table are reused by the next chunk
+      const int c = grab_chunk(work + pool, last_grab, &s_wsum[0]);
+      if (c >= NC) break;
+      f0 = p0 + (long long)c * C;
+      cnt = p1 - f0 < C ? p1 - f0 : C;
+    }
   }
 }
 
@@ -919,7 +963,7 @@ size_t mqa_ring_bytes(int variant, int slots) {
 }
 
 hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, int grid,
-                      size_t lds_bytes, hipStream_t stream) {
+                      size_t lds_bytes, WorkCounter* work, hipStream_t stream) {
   const void* fn = mqa_kernel_symbol(slots, variant, out_dtype);
   if (!fn) return hipErrorInvalidValue;
   const uint8_t* q = a.q;
@@ -930,7 +974,8 @@ hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, i
   const int32_t* bt = a.bt;
   const int32_t* sched = a.schedule;
   void* out = a.out;
-  void* args[] = {&q, &q_sf, &kv, &w, &seq_lens, &bt, &sched, &out, const_cast<MqaArgs*>(&a)};
+  void* args[] = {&q,   &q_sf, &kv,   &w,    &seq_lens,
+                  &bt,  &sched, &out, &work, const_cast<MqaArgs*>(&a)};
   return hipLaunchKernel(fn, dim3(grid), dim3(kBlockThreads), args, lds_bytes, stream);
 }
 

@@ -34,7 +34,21 @@ struct MqaArgs {
   int head_dim;            // D (bytes of an FP8 key row)
   int cus;                 // compute units of the device (split weights)
   int split_skew;          // in-call split: extra share of early dispatch rounds, 1/1024ths
+  int dyn_share;           // in-call split with a work counter: items left for dynamic
+                           // chunks, 1/1024ths of the call's items
+  int dyn_chunk;           // items per dynamic chunk
 };
+
+// Work counters of the in-call split (in the caller's workspace or the
+// library's static scratch): one per XCD, each on its own 128-byte line,
+// counting the chunk grabs of that XCD's workgroups.  Zero before a launch;
+// the launch's last grab on each XCD returns its counter to zero.
+constexpr int kXcds = 8;
+struct WorkCounter {
+  int next;
+  int pad[31];
+};
+constexpr size_t kWorkspaceBytes = kXcds * sizeof(WorkCounter);  // 1 KiB per call
 
 struct IdxArgs {
   const uint16_t* q;        // bf16 [rows, 128]; NVFP4: packed e2m1 [rows, 64]
@@ -101,6 +115,16 @@ inline int mx_kernel_variant(int sf_vec_size, int kv_sf_interleaved) {
 // launch of `slots` query slots of `variant` (measured: 4 FP8 slots, whose
 // launches are long enough for the rounds to drift apart, gain ~4%).
 inline int split_skew_for(int slots, int variant) { return slots == 4 && variant == 0 ? 300 : 0; }
+// Dynamic part of the in-call split when a work counter is given: share of
+// the call's items (1/1024ths) dealt in chunks of dyn_chunk_for items.
+// Measured (shares 0..256/1024, chunks 2..16): every setting is within
+// run-to-run noise of the static split for FP8 and slower for MXFP4 (a chunk
+// pays its own page-id and first-page round trips), so FP8 keeps a small
+// dynamic share and MXFP4 none.
+inline int dyn_share_for(int slots, int variant) {
+  return variant != 0 ? 0 : slots == 1 ? 32 : 64;
+}
+inline int dyn_chunk_for(int slots, int variant) { return variant == 0 && slots == 1 ? 2 : 4; }
 const void* mqa_kernel_symbol(int slots, int variant, int out_dtype);
 // LDS before the request prefix of a launch of `slots` query slots
 size_t mqa_ring_bytes(int variant, int slots);
@@ -119,7 +143,7 @@ const void* indexer_kernel_symbol();
 const void* indexer_nvfp4_kernel_symbol();
 
 hipError_t launch_mqa(const MqaArgs& a, int slots, int variant, int out_dtype, int grid,
-                      size_t lds_bytes, hipStream_t stream);
+                      size_t lds_bytes, WorkCounter* work, hipStream_t stream);
 hipError_t launch_schedule(const int32_t* seq_lens, int B, int next_n, int variant,
                            int max_context, int U, int cus, int skew, int32_t* sched,
                            hipStream_t stream);

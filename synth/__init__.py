@@ -507,7 +507,7 @@ def make_proxy_inputs(q_lens, k_lens, *, num_qo_heads=64, num_kv_heads=8, paged=
 SEEDS = {"tiny_fp8": 1, "indexer_bf16": 2, "decode_fp8": 3, "verify_fp8": 4, "mxfp4": 5,
          "indexer_nvfp4": 6, "verify_fp8_n8": 7, "verify_fp8_h32": 8, "verify_fp8_bf16": 4,
          "mxfp4_n4": 9, "mxfp4_sf16": 5, "mxfp4_records": 5, "mxfp4_sf16_records": 5,
-         "proxy_decode": 10, "proxy_verify": 11}
+         "proxy_decode": 10, "proxy_verify": 11, "indexer_bf16_8k": 12, "indexer_nvfp4_8k": 13}
 
 # the MXFP4 scale layouts of the mxfp4 workload: (sf_vec_size, interleaved)
 MX_LAYOUT_CONFIGS = {"mxfp4": (32, False), "mxfp4_sf16": (16, False),
@@ -551,6 +551,10 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
                  query heads over 8 KV heads (head_dim 128), paged NVFP4 keys,
                  key counts uniform in 16K..128K, causal, 1024 blocks per row
     proxy_verify the same with 4 query tokens per request
+    indexer_bf16_8k, indexer_nvfp4_8k
+                 8192 query rows in groups of 1..8 over 512 requests of up to
+                 4096 keys (64 pages each), context lengths uniform in
+                 0..4096, fp32 scores [8192, 4096]
     """
     if seed is None:
         seed = SEEDS[name]
@@ -559,6 +563,11 @@ def make_config(name: str, seed: Optional[int] = None, **overrides):
                   full_table=True, w_std=1.0)
     elif name in ("indexer_bf16", "indexer_nvfp4"):
         kw = dict(fmt="bf16" if name == "indexer_bf16" else "nvfp4")
+        kw.update(overrides)
+        return make_indexer_inputs(seed=seed, name=name, **kw)
+    elif name in ("indexer_bf16_8k", "indexer_nvfp4_8k"):
+        kw = dict(fmt="bf16" if name == "indexer_bf16_8k" else "nvfp4", rows=8192,
+                  num_requests=512, bt_width=64, max_context=4096, max_len=4096)
         kw.update(overrides)
         return make_indexer_inputs(seed=seed, name=name, **kw)
     elif name in ("proxy_decode", "proxy_verify"):

@@ -52,20 +52,20 @@ class DevMqa:
             out.view(torch.int16).fill_(BF16_SENTINEL)
         return out
 
-    def run(self, out=None, schedule=None, dtype=None, stream=None):
+    def run(self, out=None, schedule=None, dtype=None, stream=None, workspace=None):
         if out is None:
             out = self.new_out(dtype)
         m = pm()
         if self.inp.variant == "fp8":
             m.mqa_logits_fp8(self.q, self.kv, self.w, self.sl, self.bt,
                              max_context=self.inp.max_context, out=out, schedule_meta=schedule,
-                             stream=stream)
+                             stream=stream, workspace=workspace)
         else:
             m.mqa_logits_mxfp4(self.q, self.q_sf, self.kv, self.w, self.sl, self.bt,
                                sf_vec_size=self.inp.sf_vec_size,
                                is_kv_sf_interleaved=self.inp.kv_sf_interleaved,
                                max_context=self.inp.max_context, out=out,
-                               schedule_meta=schedule, stream=stream)
+                               schedule_meta=schedule, stream=stream, workspace=workspace)
         return out
 
 
@@ -195,3 +195,30 @@ def check_indexer(di, scores, what=""):
         what, int(wrote.sum()), int(written.sum()))
     # one head: A = |q.k| (weight 1, no rectifier, no s_p)
     return check_values(got[written], ref[written], np.abs(ref[written]), TOL_F32, what)
+
+
+def page_edge_cells(inp):
+    """The first and last column of every written page, for every row of
+    every request (full-size checks)."""
+    rows, cols = [], []
+    N = inp.next_n
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        T = 0 if L <= 0 else min((L + 63) // 64, inp.max_context // 64)
+        c = np.concatenate([np.arange(T) * 64, np.arange(T) * 64 + 63])
+        for t in range(N):
+            rows.append(np.full(c.size, b * N + t))
+            cols.append(c)
+    if not rows:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    return np.concatenate(rows).astype(np.int32), np.concatenate(cols).astype(np.int32)
+
+
+def check_cells(dm, out, rows, cols, what=""):
+    """Values at the given written cells against the oracle's point evaluation."""
+    inp = dm.inp
+    got, wrote = host_out(out)
+    ref, amag, w = oracle.mqa_logits_points_for(inp, rows, cols)
+    assert w.all(), "%s: a checked cell is outside the written set" % what
+    assert wrote[rows, cols].all()
+    return check_values(got[rows, cols], ref, amag, tol_for(out.dtype), what)

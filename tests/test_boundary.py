@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pmqa.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN = 0, -1, -2, -3, -4
+OK, NULL, SHAPE, UNSUP, ALIGN, WORKSPACE = 0, -1, -2, -3, -4, -5
 FAKE = 0x10000  # an aligned, never dereferenced address
 
 
@@ -42,6 +42,10 @@ def test_header_declares_the_entry_points():
         assert n in names, n
 
 
+def test_workspace_bytes(pm):
+    assert pm.workspace_bytes() == 1024  # one 128-byte counter line per XCD
+
+
 def test_library_exports_every_declared_symbol(pm):
     lib = ctypes.CDLL(pm.LIB_PATH)
     for n in declared_functions():
@@ -62,18 +66,19 @@ def test_helpers(pm):
     assert pm.min_block_table_width(200) == 4 and pm.min_block_table_width(131072) == 2048
     assert pm.schedule_ints(1) == 8 + 3 * 2
     assert pm.schedule_ints(0) == -1 and pm.schedule_ints(1 << 21) == -1
-    for s in (0, -1, -2, -3, -4, -6, 17):
+    for s in (0, -1, -2, -3, -4, -5, -6, 17):
         assert isinstance(pm.status_string(s), str)
 
 
 def _fp8(lib, **kw):
     a = dict(q=FAKE, kv=FAKE, ps=8448, npages=10, w=FAKE, sl=FAKE, bt=FAKE, bts=4, btw=4, B=2,
              N=1, H=64, D=128, out=FAKE, ors=256, maxc=256, od=0, acc=0, sched=None,
-             stream=None)
+             ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.mqa_logits_fp8(a["q"], a["kv"], a["ps"], a["npages"], a["w"], a["sl"], a["bt"],
                               a["bts"], a["btw"], a["B"], a["N"], a["H"], a["D"], a["out"],
-                              a["ors"], a["maxc"], a["od"], a["acc"], a["sched"], a["stream"])
+                              a["ors"], a["maxc"], a["od"], a["acc"], a["sched"], a["ws"],
+                              a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,rc", [
@@ -87,6 +92,9 @@ def _fp8(lib, **kw):
     (dict(bts=3), SHAPE), (dict(ors=200), SHAPE), (dict(npages=0), SHAPE),
     (dict(q=FAKE + 8), ALIGN), (dict(w=FAKE + 4), ALIGN), (dict(sl=FAKE + 2), ALIGN),
     (dict(B=0), OK), (dict(maxc=0, ors=0), OK),
+    (dict(ws=FAKE, wsb=1023), WORKSPACE), (dict(ws=FAKE, wsb=0), WORKSPACE),
+    (dict(ws=FAKE + 4, wsb=1024), ALIGN), (dict(ws=FAKE, wsb=1024, B=0), OK),
+    (dict(ws=FAKE, wsb=1 << 20, B=-1), SHAPE), (dict(ws=None, wsb=3, B=0), OK),
 ])
 def test_fp8_validation(pm, kw, rc):
     assert _fp8(pm.library(), **kw) == rc
@@ -95,12 +103,12 @@ def test_fp8_validation(pm, kw, rc):
 def _mx(lib, **kw):
     a = dict(q=FAKE, qsf=FAKE, sfv=32, inter=0, kv=FAKE, ps=4352, npages=10, w=FAKE, sl=FAKE,
              bt=FAKE, bts=4, btw=4, B=2, N=2, H=64, D=128, out=FAKE, ors=256, maxc=256, od=1,
-             sched=None, stream=None)
+             sched=None, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.mqa_logits_mxfp4(a["q"], a["qsf"], a["sfv"], a["inter"], a["kv"], a["ps"],
                                 a["npages"], a["w"], a["sl"], a["bt"], a["bts"], a["btw"], a["B"],
                                 a["N"], a["H"], a["D"], a["out"], a["ors"], a["maxc"], a["od"],
-                                a["sched"], a["stream"])
+                                a["sched"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,rc", [
@@ -108,7 +116,8 @@ def _mx(lib, **kw):
     (dict(sfv=64), UNSUP), (dict(sfv=0), UNSUP), (dict(inter=2), UNSUP), (dict(inter=-1), UNSUP),
     (dict(inter=1, B=0), OK), (dict(H=32), UNSUP), (dict(D=256), UNSUP),
     (dict(qsf=None), NULL), (dict(ps=4340), SHAPE), (dict(ps=4352 + 4), ALIGN),
-    (dict(N=9), UNSUP), (dict(B=0), OK),
+    (dict(N=9), UNSUP), (dict(B=0), OK), (dict(ws=FAKE, wsb=512), WORKSPACE),
+    (dict(ws=FAKE + 8, wsb=1024), ALIGN),
 ])
 def test_mxfp4_validation(pm, kw, rc):
     assert _mx(pm.library(), **kw) == rc

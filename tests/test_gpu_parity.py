@@ -13,8 +13,8 @@ import oracle
 import synth
 import fixtures_util
 from fixtures_util import (extent, indexer_from_case, load_golden, mqa_from_case)
-from gpu_util import (DEV, DevIndexer, DevMqa, check_dense, check_indexer, check_sampled,
-                      check_values, host_out, pm, say, tol_for)
+from gpu_util import (DEV, DevIndexer, DevMqa, check_cells, check_dense, check_indexer,
+                      check_sampled, check_values, host_out, page_edge_cells, pm, say, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -286,7 +286,8 @@ def test_indexer_nvfp4_out_of_range_page_is_nan():
 
 
 @pytest.mark.parametrize("name,mode", [
-    (n, m) for n in ("decode_fp8", "verify_fp8", "mxfp4") for m in ("in_call", "schedule")
+    (n, m) for n in ("decode_fp8", "verify_fp8", "mxfp4")
+    for m in ("in_call", "schedule", "work_counter")
 ] + [("verify_fp8_bf16", "in_call"), ("mxfp4_n4", "in_call")])
 def test_full_size_config(name, mode):
     inp = synth.make_config(name)
@@ -298,9 +299,22 @@ def test_full_size_config(name, mode):
         sched = pm().mqa_logits_schedule(dm.sl, inp.next_n,
                                          0 if inp.variant == "fp8" else 1,
                                          max_context=inp.max_context)
-    out = dm.run(schedule=sched)
-    r = check_sampled(dm, out, np.random.default_rng(7), "%s %s" % (name, mode))
-    say("%s %s max err/tol %.3g" % (name, mode, r))
+    ws = pm().workspace(DEV) if mode == "work_counter" else None
+    out = dm.run(schedule=sched, workspace=ws)
+    what = "%s %s" % (name, mode)
+    if ws is not None:
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, "the work counter was not left at zero"
+    if name == "decode_fp8":
+        # every written cell (about 0.6 M) against the dense oracle
+        r = check_dense(dm, out, what)
+        say("%s: dense, max err/tol %.3g" % (what, r))
+        return
+    r = check_sampled(dm, out, np.random.default_rng(7), what)
+    rows, cols = page_edge_cells(inp)
+    re = check_cells(dm, out, rows, cols, what + " page edges")
+    say("%s max err/tol %.3g sampled, %.3g over the first and last column of all %d pages x rows"
+        % (what, r, re, rows.size // 2))
 
 
 # ------------------------------------------------------- schedule / graphs
@@ -410,6 +424,56 @@ def test_graph_replay_with_changed_inputs(variant):
         torch.cuda.synchronize()
         dm.inp = new
         check_dense(dm, out, "%s replay %d" % (variant, rep))
+
+
+@pytest.mark.parametrize("variant,next_n", [("fp8", 1), ("fp8", 2), ("fp8", 4), ("fp8", 6),
+                                            ("mxfp4", 2), ("mxfp4", 3)])
+def test_work_counter_bit_identical_and_left_zero(variant, next_n):
+    """With a workspace the last items of the call go to whichever workgroups
+    finish first: the logits are bit-identical to the static split, and
+    every call (one or two launches) leaves the counter at zero."""
+    inp = _mid_inputs(variant, next_n, seed=320 + next_n)
+    dm = DevMqa(inp)
+    say("work counter %s N=%d" % (variant, next_n))
+    ref, wref = host_out(dm.run())
+    ws = pm().workspace(DEV)
+    for _ in range(3):
+        got, wrote = host_out(dm.run(workspace=ws))
+        assert np.array_equal(wrote, wref)
+        assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+        assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("variant", ["fp8", "mxfp4"])
+def test_graph_replay_with_work_counter(variant):
+    """A call with a workspace captured once and replayed with changed
+    inputs: every replay matches the oracle and leaves the counter at zero
+    (the graph holds no clearing of it)."""
+    inp = _graph_inputs(variant, 305)
+    dm = DevMqa(inp)
+    ws = pm().workspace(DEV)
+    out = dm.new_out()
+    dm.run(out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dm.run(out=out, workspace=ws)
+    for rep in range(3):
+        new = _graph_inputs(variant, 410 + rep)
+        dm.sl.copy_(torch.from_numpy(new.seq_lens))
+        dm.q.copy_(torch.from_numpy(new.q))
+        if new.q_sf is not None:
+            dm.q_sf.copy_(torch.from_numpy(new.q_sf))
+        dm.w.copy_(torch.from_numpy(new.weights))
+        dm.kv.copy_(torch.from_numpy(new.kv))
+        dm.bt.copy_(torch.from_numpy(new.block_table))
+        out.copy_(dm.new_out())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        dm.inp = new
+        check_dense(dm, out, "%s work-counter replay %d" % (variant, rep))
 
 
 # ------------------------------------------------------------- invariants
