@@ -130,6 +130,26 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
                    void* stream);
 
 /*
+ * mqa_logits_fp8_no_alloc - mqa_logits_fp8 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments and results, without the
+ * workspace.  The work counters (1 KiB) live in a device array of the library,
+ * one per GPU, zero when the library is loaded and left zero by every
+ * completed call; the call allocates nothing and clears nothing.  Every call
+ * on one GPU shares that array: calls that may overlap on one GPU (different
+ * streams) race on it, so such callers use mqa_logits_fp8 with a workspace
+ * each.  Errors as mqa_logits_fp8 (the first call on a device also
+ * initialises it, as mqa_logits_init).
+ */
+int mqa_logits_fp8_no_alloc(const void* q, const void* kv_fused, int64_t page_stride,
+                            int32_t num_pages, const float* weights, const int32_t* seq_lens,
+                            const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                            int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                            void* out, int64_t out_row_stride, int32_t max_context,
+                            int32_t out_dtype, int32_t acc_dtype, const int32_t* schedule,
+                            void* stream);
+
+/*
  * mqa_logits_mxfp4 - MXFP4 paged MQA logits (no s_p; block scales folded).
  * ("flashinfer.attn_scores": equation, the MXFP4 bullet, and the paragraph on
  * q_sf / sf_vec_size / is_kv_sf_interleaved, two FP4 values per byte, exactly

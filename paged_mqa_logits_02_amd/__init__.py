@@ -52,6 +52,9 @@ def _load():
                                    I32, I32, I32, P, P, SZ, P]
     lib.mqa_logits_mxfp4.argtypes = [P, P, I32, I32, P, I64, I32, P, P, P, I64, I32, I32, I32,
                                      I32, I32, P, I64, I32, I32, P, P, SZ, P]
+    lib.mqa_logits_fp8_no_alloc.argtypes = [P, P, I64, I32, P, P, P, I64, I32, I32, I32, I32,
+                                            I32, P, I64, I32, I32, I32, P, P]
+    lib.mqa_logits_fp8_no_alloc.restype = ctypes.c_int
     lib.mqa_logits_workspace_bytes.argtypes = []
     lib.mqa_logits_workspace_bytes.restype = SZ
     lib.indexer_scores.argtypes = [P, I32, I32, P, I64, I32, P, I64, I32, I32, P, P, I32, P, P,
@@ -392,6 +395,19 @@ def mqa_logits_fp8(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
     out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
                           schedule_meta, output_dtype, acc_dtype, stream, workspace)
     _check(_lib.mqa_logits_fp8(*args), "mqa_logits_fp8")
+    return out
+
+
+def mqa_logits_fp8_no_alloc(q, kv_fused, weights, seq_lens, block_table, next_n=None, *,
+                            max_context=None, out=None, schedule_meta=None,
+                            output_dtype=torch.float32, acc_dtype=torch.float32, stream=None):
+    """mqa_logits_fp8 through the entry point that allocates nothing: its work
+    counters are the library's per-GPU array (calls that overlap on one GPU
+    race on it).  Pass ``out``: out=None allocates it here, in the binding."""
+    out, args = _fp8_args(q, kv_fused, weights, seq_lens, block_table, next_n, max_context, out,
+                          schedule_meta, output_dtype, acc_dtype, stream)
+    args = args[:19] + args[21:]  # no workspace pointer and size
+    _check(_lib.mqa_logits_fp8_no_alloc(*args), "mqa_logits_fp8_no_alloc")
     return out
 
 

@@ -12,6 +12,14 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// Work counters for callers that cannot allocate a workspace
+// (mqa_logits_fp8_no_alloc): one 1 KiB array per device, zero when the code
+// object is loaded, left zero by every completed launch.  In host code this
+// name is only a stand-in: the device address comes from hipGetSymbolAddress
+// (DeviceInfo::scratch) and is the only form passed to kernels.
+static __device__ __align__(256) WorkCounter scratch[kXcds];
+static_assert(sizeof(scratch) >= kWorkspaceBytes, "scratch holds one call's work counters");
+
 struct DeviceInfo {
   bool ready = false;
   int cus = 0;
@@ -26,6 +34,7 @@ struct DeviceInfo {
   // proxy score kernels [row tiles 1, 2, 4 -> 0, 1, 2][reduce]
   int occ_proxy[3][2] = {};
   size_t static_lds_proxy[3][2] = {};
+  WorkCounter* scratch = nullptr;  // this device's copy of `scratch`
 };
 
 int proxy_nt_index(int nt) { return nt == 1 ? 0 : nt == 2 ? 1 : 2; }
@@ -82,6 +91,10 @@ int init_device(int device) {
   } else {
     d.cus = prop.multiProcessorCount;
     d.lds_per_cu = prop.maxSharedMemoryPerMultiProcessor;
+    if (hipGetSymbolAddress(reinterpret_cast<void**>(&d.scratch), HIP_SYMBOL(scratch)) !=
+            hipSuccess ||
+        d.scratch == nullptr)
+      rc = PMQA_ERR_HIP;
     // occupancy from registers (LDS is accounted per call: it depends on
     // the batch and the shape)
     for (int n = 1; n <= kFastSlots && rc == PMQA_OK; ++n)
@@ -252,6 +265,23 @@ int mqa_logits_fp8(const void* q, const void* kv_fused, int64_t page_stride, int
                  bt_stride, batch, next_n, num_heads, head_dim, PMQA_VARIANT_FP8, out,
                  out_row_stride, max_context, out_dtype, schedule,
                  static_cast<WorkCounter*>(workspace), stream);
+}
+
+int mqa_logits_fp8_no_alloc(const void* q, const void* kv_fused, int64_t page_stride,
+                            int32_t num_pages, const float* weights, const int32_t* seq_lens,
+                            const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                            int32_t batch, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                            void* out, int64_t out_row_stride, int32_t max_context,
+                            int32_t out_dtype, int32_t acc_dtype, const int32_t* schedule,
+                            void* stream) {
+  DeviceInfo* d = nullptr;
+  int rc = current_device_info(&d);
+  if (rc != PMQA_OK) return rc;
+  if (sizeof(scratch) < kWorkspaceBytes) return PMQA_ERR_WORKSPACE;
+  return mqa_logits_fp8(q, kv_fused, page_stride, num_pages, weights, seq_lens, block_table,
+                        bt_stride, bt_width, batch, next_n, num_heads, head_dim, out,
+                        out_row_stride, max_context, out_dtype, acc_dtype, schedule, d->scratch,
+                        kWorkspaceBytes, stream);
 }
 
 int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
