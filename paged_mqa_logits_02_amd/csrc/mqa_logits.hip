@@ -80,21 +80,31 @@ __host__ __device__ constexpr int mx_sfv(int var) { return var == 2 || var == 4 
 __host__ __device__ constexpr bool mx_records(int var) { return var >= 3; }
 constexpr int kMxVariants = 4;
 
-// An MXFP4 page in LDS always has the same image, whatever its layout in
-// memory: 64 packed rows of 64 bytes (16-byte chunks XOR-permuted by row, as
-// for FP8), then the 64 tokens' codes, kCodes per token.  With trailing codes
-// a wave loads its 16 rows as one 16-byte piece per lane and its tokens'
-// codes as dwords; with token records it gathers the same bytes with dword
-// loads from each record (4-byte aligned: a record is 68 or 72 bytes).
+// An MXFP4 page in LDS.  Trailing codes: 64 packed rows of 64 bytes (16-byte
+// chunks XOR-permuted by row, as for FP8), then the 64 tokens' codes, kCodes
+// per token; a wave loads its 16 rows as one 16-byte piece per lane and its
+// tokens' codes as dwords.  Token records (68 or 72 bytes, 4-byte aligned):
+// the page's bytes as they are, copied in 16-byte pieces; wave w's quarter
+// is exactly records 16w .. 16w+15, so every wave still loads the rows it
+// scores itself.  row_off / chunk_off / code_off locate a row's 16-byte chunk
+// c and its codes in either image.
 template <int SFV, bool REC> struct MxPageLayout {
   static constexpr int kRowBytes = 64;
   static constexpr int kKeyBytes = kPage * kRowBytes;  // 4096
   static constexpr int kCodes = 128 / SFV;             // e8m0 codes per token
-  static constexpr int kStageBytes = kKeyBytes + kPage * kCodes;
   static constexpr int kRecBytes = kRowBytes + kCodes;  // a token record
+  static constexpr int kStageBytes = REC ? kPage * kRecBytes : kKeyBytes + kPage * kCodes;
   static constexpr int kCodeDwords = 16 * kCodes / 4;   // a wave's tokens' codes
-  static constexpr int kLoadsPerWave = REC ? 5 : 2;
+  static constexpr int kTailPieces = kRecBytes - 64;    // records: 16-byte pieces past 64 lanes
+  static constexpr int kLoadsPerWave = 2;
+  static constexpr int kRowStride = REC ? kRecBytes : kRowBytes;   // between rows
+  static constexpr int kCodeStride = REC ? kRecBytes : kCodes;     // between rows' codes
   __device__ static int swz(int r) { return (r >> 1) & 3; }
+  __device__ static int row_off(int r) { return r * kRowStride; }
+  __device__ static int chunk_off(int r, int c) { return REC ? 16 * c : 16 * (c ^ swz(r)); }
+  __device__ static int code_off(int r) {
+    return REC ? r * kRecBytes + kRowBytes : kKeyBytes + r * kCodes;
+  }
   struct Lanes {
     uint32_t off[kLoadsPerWave];
   };
@@ -106,17 +116,9 @@ template <int SFV, bool REC> struct MxPageLayout {
       o.off[0] = r * kRowBytes + 16 * ((lane & 3) ^ swz(r));
       o.off[1] = kKeyBytes + 16 * wave * kCodes + 4 * (lane < kCodeDwords ? lane : 0);
     } else {
-      // load k of the wave's rows: LDS dword 64k + lane of its 1 KB block is
-      // byte 4e of slot s of row rr, which holds chunk s ^ swz(r) of the row
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int d = 64 * k + lane, rr = d >> 4, s = (d >> 2) & 3, e = d & 3;
-        const int r = 16 * wave + rr;
-        o.off[k] = r * kRecBytes + 16 * (s ^ swz(r)) + 4 * e;
-      }
-      const int c = lane < kCodeDwords ? lane : 0;  // code dword c of the wave's tokens
-      const int r = 16 * wave + c / (kCodes / 4);
-      o.off[4] = r * kRecBytes + kRowBytes + 4 * (c % (kCodes / 4));
+      const int base = 16 * wave * kRecBytes;
+      o.off[0] = base + 16 * lane;
+      o.off[1] = base + 16 * (64 + (lane < kTailPieces ? lane : 0));
     }
     return o;
   }
@@ -126,12 +128,24 @@ template <int SFV, bool REC> struct MxPageLayout {
       dma16_page(page + o.off[0], stage + 16 * wave * kRowBytes);
       if (lane < kCodeDwords) dma4_page(page + o.off[1], stage + kKeyBytes + 16 * wave * kCodes);
     } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) dma4_page(page + o.off[k], stage + 16 * wave * kRowBytes + 256 * k);
-      if (lane < kCodeDwords) dma4_page(page + o.off[4], stage + kKeyBytes + 16 * wave * kCodes);
+      dma16_page(page + o.off[0], stage + 16 * wave * kRecBytes);
+      if (lane < kTailPieces) dma16_page(page + o.off[1], stage + 16 * wave * kRecBytes + 1024);
     }
   }
 };
+
+// 16 bytes from LDS: 16-byte aligned (one 128-bit read), or only 4-byte
+// aligned in token records (two 64-bit-pair reads).
+typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
+template <bool A4>
+__device__ __forceinline__ v4i lds16(const uint8_t* p) {
+  if constexpr (A4) {
+    return *reinterpret_cast<const v4i_a4*>(p);
+  } else {
+    return *reinterpret_cast<const v4i*>(p);
+  }
+}
+
 template <> struct PageLayout<1> : MxPageLayout<32, false> {};
 template <> struct PageLayout<2> : MxPageLayout<16, false> {};
 template <> struct PageLayout<3> : MxPageLayout<32, true> {};
@@ -140,7 +154,7 @@ template <> struct PageLayout<4> : MxPageLayout<16, true> {};
 // MXFP4 operand fragment (16x16x128 tiles): lane l holds the 32-element block
 // g = l>>4 of its row (16 packed bytes) and its codes: one (sf) per 32 values,
 // or one per 16 (sf for the first half, sf2 for the second).
-template <int SFV> struct MxFrag {
+template <int SFV, bool REC = false> struct MxFrag {
   static constexpr int kCodes = 128 / SFV;
   v4i v;
   int sf, sf2;
@@ -153,9 +167,9 @@ template <int SFV> struct MxFrag {
     if constexpr (SFV == 16) sf2 = ldg_untracked_u8(codes + 2 * g + 1);
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int g) {
-    using L = MxPageLayout<SFV, false>;
-    v = *reinterpret_cast<const v4i*>(stage + r * L::kRowBytes + 16 * (g ^ L::swz(r)));
-    const uint8_t* codes = stage + L::kKeyBytes + r * kCodes;
+    using L = MxPageLayout<SFV, REC>;
+    v = lds16<REC>(stage + L::row_off(r) + L::chunk_off(r, g));
+    const uint8_t* codes = stage + L::code_off(r);
     sf = codes[SFV == 32 ? g : 2 * g];
     if constexpr (SFV == 16) sf2 = codes[2 * g + 1];
   }
@@ -164,10 +178,10 @@ template <int SFV> struct MxFrag {
     if constexpr (SFV == 16) settle(sf2);
   }
 };
-template <> struct Frag<1> : MxFrag<32> {};
-template <> struct Frag<2> : MxFrag<16> {};
-template <> struct Frag<3> : MxFrag<32> {};
-template <> struct Frag<4> : MxFrag<16> {};
+template <> struct Frag<1> : MxFrag<32, false> {};
+template <> struct Frag<2> : MxFrag<16, false> {};
+template <> struct Frag<3> : MxFrag<32, true> {};
+template <> struct Frag<4> : MxFrag<16, true> {};
 
 // Operands of the MXFP4 products.  A key fragment is multiplied as loaded.  A
 // query fragment with one code per 32 values is too; with one code per 16
@@ -185,15 +199,23 @@ template <class F>
 __device__ __forceinline__ MxSplitQuery split_query(const F& f) {
   return MxSplitQuery{(v4i){f.v[0], f.v[1], 0, 0}, (v4i){0, 0, f.v[2], f.v[3]}, f.sf, f.sf2};
 }
-__device__ __forceinline__ const MxFrag<32>& query_operand(const MxFrag<32>& f) { return f; }
-__device__ __forceinline__ MxSplitQuery query_operand(const MxFrag<16>& f) { return split_query(f); }
-template <int SFV>
-__device__ __forceinline__ const MxFrag<SFV>& key_operand(const MxFrag<SFV>& k) { return k; }
+template <bool R>
+__device__ __forceinline__ const MxFrag<32, R>& query_operand(const MxFrag<32, R>& f) {
+  return f;
+}
+template <bool R>
+__device__ __forceinline__ MxSplitQuery query_operand(const MxFrag<16, R>& f) {
+  return split_query(f);
+}
+template <int SFV, bool R>
+__device__ __forceinline__ const MxFrag<SFV, R>& key_operand(const MxFrag<SFV, R>& k) { return k; }
 
-__device__ __forceinline__ v4f mma(const MxFrag<32>& q, const MxFrag<32>& k) {
+template <bool R>
+__device__ __forceinline__ v4f mma(const MxFrag<32, R>& q, const MxFrag<32, R>& k) {
   return mfma_fp4(q.v, q.sf, k.v, k.sf, (v4f){0.f, 0.f, 0.f, 0.f});
 }
-__device__ __forceinline__ v4f mma(const MxSplitQuery& q, const MxFrag<16>& k) {
+template <bool R>
+__device__ __forceinline__ v4f mma(const MxSplitQuery& q, const MxFrag<16, R>& k) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   return mfma_fp4(q.hi, q.sf2, k.v, k.sf2, mfma_fp4(q.lo, q.sf, k.v, k.sf, z));
 }
@@ -218,7 +240,7 @@ template <int VAR> struct WideFrag;
 
 // MXFP4: lane l holds 32-element block c = 2ks + h of the row (16 packed bytes)
 // and its code(s), as MxFrag.
-template <int SFV> struct MxWideFrag {
+template <int SFV, bool REC = false> struct MxWideFrag {
   static constexpr int kCodes = 128 / SFV;
   v4i v;
   int sf, sf2;
@@ -231,10 +253,10 @@ template <int SFV> struct MxWideFrag {
     if constexpr (SFV == 16) sf2 = ldg_untracked_u8(codes + 2 * c + 1);
   }
   __device__ __forceinline__ void load_stage(const uint8_t* stage, int r, int ks, int h) {
-    using L = MxPageLayout<SFV, false>;
+    using L = MxPageLayout<SFV, REC>;
     const int c = 2 * ks + h;
-    v = *reinterpret_cast<const v4i*>(stage + r * L::kRowBytes + 16 * (c ^ L::swz(r)));
-    const uint8_t* codes = stage + L::kKeyBytes + r * kCodes;
+    v = lds16<REC>(stage + L::row_off(r) + L::chunk_off(r, c));
+    const uint8_t* codes = stage + L::code_off(r);
     sf = codes[SFV == 32 ? c : 2 * c];
     if constexpr (SFV == 16) sf2 = codes[2 * c + 1];
   }
@@ -243,22 +265,26 @@ template <int SFV> struct MxWideFrag {
     if constexpr (SFV == 16) settle(sf2);
   }
 };
-template <> struct WideFrag<1> : MxWideFrag<32> {};
-template <> struct WideFrag<2> : MxWideFrag<16> {};
-template <> struct WideFrag<3> : MxWideFrag<32> {};
-template <> struct WideFrag<4> : MxWideFrag<16> {};
+template <> struct WideFrag<1> : MxWideFrag<32, false> {};
+template <> struct WideFrag<2> : MxWideFrag<16, false> {};
+template <> struct WideFrag<3> : MxWideFrag<32, true> {};
+template <> struct WideFrag<4> : MxWideFrag<16, true> {};
 
-__device__ __forceinline__ const MxWideFrag<32>& query_operand(const MxWideFrag<32>& f) {
+template <bool R>
+__device__ __forceinline__ const MxWideFrag<32, R>& query_operand(const MxWideFrag<32, R>& f) {
   return f;
 }
-__device__ __forceinline__ MxSplitQuery query_operand(const MxWideFrag<16>& f) {
+template <bool R>
+__device__ __forceinline__ MxSplitQuery query_operand(const MxWideFrag<16, R>& f) {
   return split_query(f);
 }
-__device__ __forceinline__ v16f mma_wide(const MxWideFrag<32>& q, const MxWideFrag<32>& k,
+template <bool R>
+__device__ __forceinline__ v16f mma_wide(const MxWideFrag<32, R>& q, const MxWideFrag<32, R>& k,
                                          const v16f& c) {
   return mfma32_fp4(q.v, q.sf, k.v, k.sf, c);
 }
-__device__ __forceinline__ v16f mma_wide(const MxSplitQuery& q, const MxWideFrag<16>& k,
+template <bool R>
+__device__ __forceinline__ v16f mma_wide(const MxSplitQuery& q, const MxWideFrag<16, R>& k,
                                          const v16f& c) {
   return mfma32_fp4(q.hi, q.sf2, k.v, k.sf2, mfma32_fp4(q.lo, q.sf, k.v, k.sf, c));
 }
@@ -560,7 +586,8 @@ __device__ __forceinline__ void load_red_query(RedQuery<TW, VAR>& qf, const MqaA
 }
 
 // MXFP4: the lane's key and code addresses of sub-tile 0 (rows from 16 s0),
-// computed once per page; sub-tile s adds s * 1024 / s * 16 * kCodes.  The
+// computed once per page; sub-tile s adds 16 s rows of each (16 s * kRowStride
+// / 16 s * kCodeStride bytes).  The
 // empty asm makes the two bases opaque, so the compiler keeps them as bases
 // with the sub-tile constant in the offset field (rather than hoisting one
 // lane offset per sub-tile and adding the page base to each).
@@ -572,16 +599,20 @@ struct Fp4SubtileBase {
   lds_ptr key, scale;
   __device__ __forceinline__ Fp4SubtileBase(const uint8_t* stage, int s0, int rr, int g) {
     const lds_ptr st = (lds_ptr)stage;
-    key = st + (16 * s0 + rr) * L::kRowBytes + 16 * (g ^ L::swz(rr));
-    scale = st + L::kKeyBytes + (16 * s0 + rr) * kCodes + (kCodes == 4 ? g : 2 * g);
+    key = st + L::row_off(16 * s0 + rr) + L::chunk_off(rr, g);
+    scale = st + L::code_off(16 * s0 + rr) + (kCodes == 4 ? g : 2 * g);
     asm("" : "+v"(key));
     asm("" : "+v"(scale));
   }
+  typedef __attribute__((address_space(3))) const v4i_a4* lds_v4i_a4;
+  typedef __attribute__((address_space(3))) const v4i* lds_v4i;
   __device__ __forceinline__ void load(Frag<VAR>& f, int s) const {
-    f.v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
-        key + 16 * s * L::kRowBytes);
-    f.sf = scale[16 * s * kCodes];
-    if constexpr (kCodes == 8) f.sf2 = scale[16 * s * kCodes + 1];
+    if constexpr (L::kRowStride % 16 == 0)
+      f.v = *reinterpret_cast<lds_v4i>(key + 16 * s * L::kRowStride);
+    else
+      f.v = *reinterpret_cast<lds_v4i_a4>(key + 16 * s * L::kRowStride);
+    f.sf = scale[16 * s * L::kCodeStride];
+    if constexpr (kCodes == 8) f.sf2 = scale[16 * s * L::kCodeStride + 1];
   }
 };
 
