@@ -105,22 +105,34 @@ KERNEL_SOURCES = ["paged_mqa_logits_02_amd/csrc/mqa_logits.hip",
                   "paged_mqa_logits_02_amd/build.py"]
 
 
-def kernel_source_hash():
-    """sha256 over the logits kernel's sources and build flags."""
+# the sources of the other kernels' profiles (proxy score, indexer)
+KERNEL_SOURCES_OF = {
+    "mqa_logits": KERNEL_SOURCES,
+    "proxy": ["paged_mqa_logits_02_amd/csrc/proxy.hip", "paged_mqa_logits_02_amd/csrc/device.hpp",
+              "paged_mqa_logits_02_amd/csrc/pmqa_internal.h", "paged_mqa_logits_02_amd/build.py"],
+    "indexer": ["paged_mqa_logits_02_amd/csrc/indexer.hip",
+                "paged_mqa_logits_02_amd/csrc/device.hpp",
+                "paged_mqa_logits_02_amd/csrc/pmqa_internal.h",
+                "paged_mqa_logits_02_amd/build.py"],
+}
+
+
+def kernel_source_hash(kernel="mqa_logits"):
+    """sha256 over a kernel's sources and build flags."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES_OF[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counter_traffic(workload):
+def counter_traffic(workload, kernel="mqa_logits"):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
     for a plain copy of known size); None if there is none or it was taken on
     other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "mqa_logits_%s_traffic.txt" % workload)
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -129,7 +141,7 @@ def counter_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -167,9 +179,23 @@ def cpu_baseline(inp, target_s=12.0):
         npos = int(min(max(rate * (target_s - spent), 256), 4_000_000))
         if target_s - spent < 0.5:
             break
+    # the same oracle on one thread, on a short sample (about 3 s)
+    done1, spent1, npos = 0, 0.0, 64
+    while spent1 < 3.0:
+        rows, cols = sample(npos)
+        t0 = time.perf_counter()
+        oracle.mqa_logits_points_for(inp, rows, cols, nthreads=1)
+        dt = time.perf_counter() - t0
+        done1 += npos
+        spent1 += dt
+        npos = int(min(max(npos / max(dt, 1e-6) * (3.0 - spent1), 64), 1_000_000))
+        if 3.0 - spent1 < 0.2:
+            break
     return {"value": done / spent, "unit": "KV positions/s", "cores": threads, "kind": "oracle",
             "sample": "%d random KV positions of the workload x all %d query slots, float64 "
-                      "oracle at sampled cells, %.1f s" % (done, inp.next_n, spent)}
+                      "oracle at sampled cells, %.1f s" % (done, inp.next_n, spent),
+            "single_thread_value": done1 / spent1,
+            "single_thread_sample": "%d random KV positions, 1 thread, %.1f s" % (done1, spent1)}
 
 
 def copy_calibration(steps):
@@ -267,6 +293,8 @@ def run_indexer(args, torch, synth, pm, dev):
     alg = int((lens_np * (key_b + 4 * sizes)).sum())
     positions = int(lens_np.sum())
     achieved = alg / (kern * 1e-3) / 1e9
+    traffic = counter_traffic(args.workload, "indexer")
+    traffic_gbs = None if traffic is None else traffic / (kern * 1e-3) / 1e9
     line = {
         "metric": METRIC_INDEXER_NVFP4 if nvfp4 else METRIC_INDEXER,
         "value": positions * K / (total_ms * 1e-3),
@@ -278,9 +306,9 @@ def run_indexer(args, torch, synth, pm, dev):
                    "rows": inp.rows, "groups": inp.groups, "max_context": inp.max_context,
                    "kv_positions": positions, "key_replicas": R, "kernel_ms_avg": kern,
                    "timing": "host launches of prepared calls, events around the %d launches" % K,
-                   "algorithmic_bytes_per_launch": alg},
+                   "algorithmic_bytes_per_launch": alg, "counter_bytes_per_launch": traffic},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_gbs},
     }
     print(json.dumps(line), flush=True)
 
@@ -347,10 +375,13 @@ def run_proxy(args, torch, synth, pm, dev):
     alg, flops, positions = proxy_bytes_and_flops(inp)
     achieved = alg / (kern * 1e-3) / 1e9
     tflops = flops / (kern * 1e-3) / 1e12
+    traffic = counter_traffic(args.workload, "proxy")
+    traffic_gbs = None if traffic is None else traffic / (kern * 1e-3) / 1e9
     hbm = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+           "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_gbs}
     mfma = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
-            "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None}
+            "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": traffic_gbs,
+            "traffic_unit": "GB/s of HBM counter bytes"}
     hbm_s, mfma_s = alg / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS["f16"] * 1e12)
     line = {
         "metric": METRIC_PROXY % (inp.num_qo_heads, inp.num_kv_heads),
@@ -364,6 +395,7 @@ def run_proxy(args, torch, synth, pm, dev):
                    "products": "f16 MFMA of exactly dequantised e2m1 x e4m3, fp32 sums",
                    "timing": "host launches of prepared calls, events around the %d launches" % K,
                    "algorithmic_bytes_per_launch": alg, "flops_per_launch": flops,
+                   "counter_bytes_per_launch": traffic,
                    "hbm": dict(hbm, ideal_us=hbm_s * 1e6), "mfma": dict(mfma, ideal_us=mfma_s * 1e6)},
         "roofline": mfma if mfma_s > hbm_s else hbm,
     }

@@ -63,7 +63,7 @@ def test_counter_traffic_only_for_current_sources(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel="mqa_logits": "abc")
     path = prof / "mqa_logits_w_traffic.txt"
     assert bench.counter_traffic("w") is None
     path.write_text("# comment: x\nkernel_source_sha256: abc\ntraffic_bytes_per_launch: 1234\n")
