@@ -135,12 +135,16 @@ template <int SFV, bool REC> struct MxPageLayout {
 };
 
 // 16 bytes from LDS: 16-byte aligned (one 128-bit read), or only 4-byte
-// aligned in token records (two 64-bit-pair reads).
-typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
+// aligned in token records: four dword reads, which the compiler pairs.
+// (A 4-byte aligned vector load is split without the memory information the
+// compiler needs to tell it from the page loads into LDS still in flight, so
+// it would wait for all of them before every page.)
 template <bool A4>
 __device__ __forceinline__ v4i lds16(const uint8_t* p) {
   if constexpr (A4) {
-    return *reinterpret_cast<const v4i_a4*>(p);
+    typedef __attribute__((address_space(3))) const int* lds_int;
+    const lds_int q = (lds_int)p;
+    return (v4i){q[0], q[1], q[2], q[3]};
   } else {
     return *reinterpret_cast<const v4i*>(p);
   }
@@ -604,13 +608,15 @@ struct Fp4SubtileBase {
     asm("" : "+v"(key));
     asm("" : "+v"(scale));
   }
-  typedef __attribute__((address_space(3))) const v4i_a4* lds_v4i_a4;
   typedef __attribute__((address_space(3))) const v4i* lds_v4i;
   __device__ __forceinline__ void load(Frag<VAR>& f, int s) const {
-    if constexpr (L::kRowStride % 16 == 0)
+    if constexpr (L::kRowStride % 16 == 0) {
       f.v = *reinterpret_cast<lds_v4i>(key + 16 * s * L::kRowStride);
-    else
-      f.v = *reinterpret_cast<lds_v4i_a4>(key + 16 * s * L::kRowStride);
+    } else {
+      typedef __attribute__((address_space(3))) const int* lds_int;
+      const lds_int q = (lds_int)(key + 16 * s * L::kRowStride);
+      f.v = (v4i){q[0], q[1], q[2], q[3]};
+    }
     f.sf = scale[16 * s * L::kCodeStride];
     if constexpr (kCodes == 8) f.sf2 = scale[16 * s * L::kCodeStride + 1];
   }
