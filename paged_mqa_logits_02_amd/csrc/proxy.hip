@@ -24,10 +24,12 @@
 // row l & 15: the block max is a running element-wise max over the eight
 // key tiles, then a max over the four 16-lane rows.  Each wave takes a
 // contiguous range of units (units of one request and KV head are adjacent,
-// so the query rows are reused across blocks); as each key tile of a unit is
-// dequantised its registers are refilled with that tile of the next unit, so
-// the next unit's keys load while the current one is scored, and page ids are
-// read 64 units ahead (one per lane).  With reduce_heads the units of one (token
+// so the query rows are reused across blocks).  Each wave has a private 9 KB
+// LDS slot: at the start of a unit it copies the slot (that unit's keys and
+// scales) into registers and at once loads the whole next unit into the slot
+// with direct-to-LDS copies, so a full unit is in flight while one is scored
+// (a unit's 9 KB, 12 waves per CU); page ids are read 64 units ahead (one per
+// lane).  With reduce_heads the units of one (token
 // chunk, block) run over the KV heads consecutively and the wave keeps the
 // per-token max across them.  Blocks past a request's last visible one are
 // never read: a final sweep writes their -inf (and every output of a token
@@ -273,44 +275,69 @@ __device__ __forceinline__ void issue_query(const ProxyArgs& a, const Unit& u,
   }
 }
 
-// Where a unit's keys are: uniform bases of its block's packed rows and
-// scale rows, the byte distance between consecutive keys' rows, and (flat
-// keys) the last key of the block that exists.
-struct KeySrc {
-  const uint8_t* kb;
-  const uint8_t* sb;
-  uint32_t kstride, sstride;
-  int last;  // largest key index within the block to read (-1: read nothing)
-};
-__device__ __forceinline__ KeySrc key_src(const ProxyArgs& a, const Unit& u, int pid) {
-  KeySrc ks;
-  if (a.paged) {
-    const long long page = (pid >= 0 && pid < a.num_pages) ? pid : 0;
-    ks.kb = a.k + page * a.page_stride + (long long)u.j * kBlk * 64;
-    ks.sb = a.ks + ((page * a.hkv + u.j) * kBlk) * 8;
-    ks.kstride = 64;
-    ks.sstride = 8;
-    ks.last = kBlk - 1;
-  } else {
-    const long long first = u.q.bad ? 0 : u.q.kbase + (long long)kBlk * u.t;
-    const long long row = first * a.hkv + u.j;
-    ks.kb = a.k + row * 64;
-    ks.sb = a.ks + row * 8;
-    ks.kstride = 64u * a.hkv;
-    ks.sstride = 8u * a.hkv;
-    ks.last = u.q.bad ? -1 : min(kBlk - 1, u.q.lk - 1 - kBlk * u.t);
-  }
-  return ks;
+// A wave's LDS slot: the unit's 128 packed key rows (64 B each, the 16-byte
+// chunk c of row r stored at chunk position c ^ ((r >> 2) & 3), so that the
+// operand reads of 16 rows x 4 chunks meet every bank once per 16 lanes), then
+// their 128 scale rows of 8 bytes.
+constexpr int kSlotKeyBytes = kBlk * 64;
+constexpr int kSlotBytes = kSlotKeyBytes + kBlk * 8;  // 9 KB
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 16, 0, 2);  // non-temporal
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 4, 0, 2);
 }
 
-// Loads key tile s (16 keys) of a unit into raw.
+// Loads unit u's keys and scales into the slot (every lane of the wave).
+// Load i of the keys fills slot bytes 1024 i + 16 lane: row 16 i + lane / 4,
+// chunk position lane % 4, which holds chunk (lane % 4) ^ ((lane >> 4) & 3)
+// of that row.  Paged: the block's rows and scale rows are contiguous; flat:
+// rows lie Hkv rows apart and rows past the request's last key repeat it.
+__device__ __forceinline__ void issue_unit(const ProxyArgs& a, const Unit& u, int pid,
+                                           uint8_t* slot, int lane) {
+  const int rr = lane >> 2, pos = lane & 3;
+  const uint32_t kchunk = 16u * (uint32_t)(pos ^ ((lane >> 4) & 3));
+  if (a.paged) {
+    const long long page = (pid >= 0 && pid < a.num_pages) ? pid : 0;
+    const uint8_t* kb = a.k + page * a.page_stride + (long long)u.j * kBlk * 64;
+    const uint8_t* sb = a.ks + ((page * a.hkv + u.j) * kBlk) * 8;
+    const uint32_t lo = (uint32_t)rr * 64u + kchunk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(kb + 1024u * i + lo, slot + 1024 * i);
+    dma16(sb + 16u * lane, slot + kSlotKeyBytes);
+  } else {
+    if (u.q.bad) return;  // keys outside the buffer: never read (outputs NaN)
+    const long long first = u.q.kbase + (long long)kBlk * u.t;
+    const int last = min(kBlk - 1, u.q.lk - 1 - kBlk * u.t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const long long row = first + min(16 * i + rr, last);
+      dma16(a.k + (row * a.hkv + u.j) * 64 + kchunk, slot + 1024 * i);
+    }
+    // scale rows: dword (lane & 1) of row 32 i + lane / 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long long row = first + min(32 * i + (lane >> 1), last);
+      dma4(a.ks + (row * a.hkv + u.j) * 8 + 4 * (lane & 1), slot + kSlotKeyBytes + 256 * i);
+    }
+  }
+}
+
+// The lane's operands of all eight key tiles from the slot.
 template <int NT>
-__device__ __forceinline__ void issue_key_tile(const KeySrc& src, int s, Raw<NT>& raw, int lane) {
-  if (src.last < 0) return;  // keys outside the buffer: never read (outputs NaN)
-  const int g = lane >> 4, cl = lane & 15;
-  const uint32_t key = (uint32_t)min(16 * s + cl, src.last);
-  raw.k[s] = ldg_stream<v4i>(src.kb + (key * src.kstride + 16u * g));
-  raw.ks[s] = ldg<uint16_t>(src.sb + (key * src.sstride + 2u * g));
+__device__ __forceinline__ void read_slot(const uint8_t* slot, Raw<NT>& raw, int lane) {
+  typedef __attribute__((address_space(3))) const v4i* lds_v4i;
+  typedef __attribute__((address_space(3))) const uint16_t* lds_u16;
+  const int g = lane >> 4, c = lane & 15;
+  const int kpos = 16 * (g ^ ((c >> 2) & 3));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int row = 16 * s + c;
+    raw.k[s] = *(lds_v4i)(slot + row * 64 + kpos);
+    raw.ks[s] = *(lds_u16)(slot + kSlotKeyBytes + row * 8 + 2 * g);
+  }
 }
 
 // Eight values of one packed dword times the f16 scale pair s (both halves
@@ -363,14 +390,11 @@ __device__ __forceinline__ void dequant_query(const ProxyArgs& a, const Unit& u,
 
 // Scores one unit: per row tile, the lane ends with the block max of query
 // row (lane & 15) (scaled by |g|; -inf if no key is visible; NaN if the
-// block's page id is out of range and a key is visible).  As each key tile is
-// dequantised, its registers are refilled with the same tile of the next
-// unit (if has_next), so the next unit's keys load while this one is scored.
+// block's page id is out of range and a key is visible).
 template <int NT>
 __device__ __forceinline__ void score_unit(const ProxyArgs& a, const Unit& u, int pid,
-                                           const LaneRows<NT>& lr, Raw<NT>& raw,
-                                           const Query<NT>& qf, bool has_next,
-                                           const KeySrc& next_src, int lane, float res[NT]) {
+                                           const LaneRows<NT>& lr, const Raw<NT>& raw,
+                                           const Query<NT>& qf, int lane, float res[NT]) {
   const int g = lane >> 4;
   const float ninf = -__builtin_inff();
   int lim[NT];  // the lane's largest visible key index, per row tile
@@ -392,7 +416,6 @@ __device__ __forceinline__ void score_unit(const ProxyArgs& a, const Unit& u, in
   for (int s = 0; s < 8; ++s) {
     v8h ka[4];
     dequant32(raw.k[s], raw.ks[s], (_Float16)1.0f, ka);
-    if (has_next) issue_key_tile(next_src, s, raw, lane);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -426,7 +449,7 @@ __device__ __forceinline__ void score_unit(const ProxyArgs& a, const Unit& u, in
 
 template <int NT, bool RED>
 __device__ void run_units(const ProxyArgs& a, const int* s_prefix, const int* s_tiles,
-                          float* s_red, int f0, int count, int lane) {
+                          float* s_red, uint8_t* slot, int f0, int count, int lane) {
   if (count <= 0) return;
   const int f_end = f0 + count;
   Unit u;
@@ -442,15 +465,23 @@ __device__ void run_units(const ProxyArgs& a, const int* s_prefix, const int* s_
   Query<NT> qf;
   int pid = __builtin_amdgcn_readfirstlane(pidv);
   issue_query(a, u, lr, raw, lane);
-  {
-    const KeySrc src = key_src(a, u, pid);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) issue_key_tile(src, s, raw, lane);
-  }
+  issue_unit(a, u, pid, slot, lane);
   bool newq = true;
   // reduce_heads: per-token running max (lane = token of the chunk) and NaN flag
   float tok_max = -__builtin_inff();
   bool tok_nan = false;
+  // A unit's results are stored one unit later, after the next unit's loads
+  // are issued: the wait at the start of each unit then finds them long done.
+  float pval[NT];
+  long long pidx[NT];
+  bool pvalid[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) pvalid[nt] = false;
+  auto flush = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (pvalid[nt]) a.out[pidx[nt]] = pval[nt];
+  };
 
   for (int n = 0; n < count; ++n) {
     const bool has_next = n + 1 < count;
@@ -462,20 +493,27 @@ __device__ void run_units(const ProxyArgs& a, const int* s_prefix, const int* s_
     }
     const int pid_next = __builtin_amdgcn_readlane(pidv, (n + 1) & 63);
     const bool newq_next = has_next && (un.r != u.r || un.j != u.j || un.c != u.c);
+    // this unit's keys (and query rows, if new) have landed: into registers,
+    // then the next unit into the slot
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt untouched
+    asm volatile("" ::: "memory");
+    read_slot(slot, raw, lane);
     if (newq) dequant_query(a, u, lr, raw, qf);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt untouched: the slot reads are done
+    asm volatile("" ::: "memory");
     if (newq_next) issue_query(a, un, lr, raw, lane);
+    if (has_next) issue_unit(a, un, pid_next, slot, lane);
+    flush();
     float res[NT];
-    score_unit(a, u, pid, lr, raw, qf, has_next, key_src(a, un, pid_next), lane, res);
+    score_unit(a, u, pid, lr, raw, qf, lane, res);
     if constexpr (!RED) {
-      if (lane < kRows) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const RowOf ro = row_of_lane(a, u, lr, nt);
-          if (ro.valid) {
-            const long long h = (long long)u.j * a.group + ro.hg;
-            a.out[(h * a.max_k_tiles + u.t) * a.total_q + u.q.q0 + ro.p] = res[nt];
-          }
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        const RowOf ro = row_of_lane(a, u, lr, nt);
+        const long long h = (long long)u.j * a.group + ro.hg;
+        pvalid[nt] = lane < kRows && ro.valid;
+        pidx[nt] = (h * a.max_k_tiles + u.t) * a.total_q + u.q.q0 + ro.p;
+        pval[nt] = res[nt];
       }
     } else {
       // rows to LDS, then lane tk combines the group's rows of token tk
@@ -492,10 +530,13 @@ __device__ void run_units(const ProxyArgs& a, const int* s_prefix, const int* s_
         }
       }
       asm volatile("" ::: "memory");
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pvalid[nt] = false;
       if (u.j == a.hkv - 1) {
         const int p = u.c * a.tc + lane;
-        if (lane < a.tc && p < u.q.lq)
-          a.out[(long long)u.t * a.total_q + u.q.q0 + p] = tok_nan ? __builtin_nanf("") : tok_max;
+        pvalid[0] = lane < a.tc && p < u.q.lq;
+        pidx[0] = (long long)u.t * a.total_q + u.q.q0 + p;
+        pval[0] = tok_nan ? __builtin_nanf("") : tok_max;
         tok_max = -__builtin_inff();
         tok_nan = false;
       }
@@ -504,6 +545,7 @@ __device__ void run_units(const ProxyArgs& a, const int* s_prefix, const int* s_
     pid = pid_next;
     newq = newq_next;
   }
+  flush();
 }
 
 // -inf for every output no unit writes: blocks at or past a request's
@@ -549,9 +591,10 @@ __global__ void __launch_bounds__(256) proxy_kernel(const ProxyArgs a) {
   extern __shared__ int smem[];
   __shared__ int s_wsum[kBlockThreads / kWave];
   __shared__ float s_red[kBlockThreads / kWave][kRows * 4];
-  int* s_cuq = smem;
-  int* s_tiles = smem + a.batch + 1;
-  int* s_prefix = smem + 2 * a.batch + 1;
+  uint8_t* slots = reinterpret_cast<uint8_t*>(smem);  // 4 waves x kSlotBytes
+  int* s_cuq = smem + 4 * kSlotBytes / 4;
+  int* s_tiles = s_cuq + a.batch + 1;
+  int* s_prefix = s_cuq + 2 * a.batch + 1;
   build_tables(a, s_cuq, s_tiles, s_prefix, s_wsum);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -566,7 +609,8 @@ __global__ void __launch_bounds__(256) proxy_kernel(const ProxyArgs a) {
   const long long step = RED ? a.hkv : 1;
   const long long items = P / step;
   const long long f0 = step * (items * w / W), f1 = step * (items * (w + 1) / W);
-  run_units<NT, RED>(a, s_prefix, s_tiles, s_red[wave], (int)f0, (int)(f1 - f0), lane);
+  run_units<NT, RED>(a, s_prefix, s_tiles, s_red[wave], slots + wave * kSlotBytes, (int)f0,
+                     (int)(f1 - f0), lane);
 
   const long long hout = RED ? 1 : a.hq;
   const long long F = hout * a.max_k_tiles * ((a.total_q + 63) / 64);
@@ -589,7 +633,7 @@ const void* proxy_kernel_symbol(int nt, int reduce) {
   }
 }
 
-size_t proxy_lds_bytes(int batch) { return (size_t)(3 * batch + 2) * sizeof(int); }
+size_t proxy_lds_bytes(int batch) { return 4 * kSlotBytes + (size_t)(3 * batch + 2) * sizeof(int); }
 
 hipError_t launch_proxy(const ProxyArgs& a, int nt, int grid, hipStream_t stream) {
   const void* fn = proxy_kernel_symbol(nt, a.reduce);
