@@ -152,11 +152,6 @@ __device__ __forceinline__ T ldg(const void* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
-template <typename T>
-__device__ __forceinline__ T ldg_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-}
-
 // Wave-wide inclusive prefix sum (64 lanes).
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll

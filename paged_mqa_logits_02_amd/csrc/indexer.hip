@@ -72,7 +72,11 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
   for (int ks = 0; ks < 4; ++ks) qa[ks] = ldg<v8bf>(a.q + qrow * 128 + 32 * ks + 8 * kg);
 
   // B: all four 16-token tiles of the page at once; an out-of-range page id
-  // reads page 0 instead and its scores are written as NaN.
+  // reads page 0 instead and its scores are written as NaN.  Each load
+  // instruction covers 64 bytes of 16 rows, so two consecutive instructions
+  // read the two halves of each 128-byte line: the loads keep the default
+  // (temporal) policy, under which the second finds the line the first
+  // brought into L2 (with non-temporal loads L2 fetched ~1.5 lines per line).
   bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
   const uint16_t* keys =
       reinterpret_cast<const uint16_t*>(a.kc + (long long)(bad ? 0 : pg) * a.page_stride);
@@ -81,7 +85,7 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kb[s][ks] = ldg_stream<v8bf>(keys + (16 * s + r) * 128 + 32 * ks + 8 * kg);
+      kb[s][ks] = ldg<v8bf>(keys + (16 * s + r) * 128 + 32 * ks + 8 * kg);
 
   if (r >= m.G) {
 #pragma unroll
@@ -169,7 +173,7 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int key = 16 * s + r;
-    kpacked[s] = ldg_stream<v4i>(page + key * 64 + 16 * kg);
+    kpacked[s] = ldg<v4i>(page + key * 64 + 16 * kg);
     ksc[s] = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
   }
 
