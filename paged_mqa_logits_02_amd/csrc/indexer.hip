@@ -17,18 +17,23 @@ namespace pmqa {
 // The group of wave (g, page pi): length, first row, row count and block-table
 // row, read together (one round trip; every read is in bounds for g < groups,
 // and the request is used only after the length check, so a length-0 group's
-// request may hold any value).  Returns false if the wave has nothing to do.
+// request may hold any value).  The empty asm uses all four values at once, so
+// the compiler cannot sink the request's read below the length check (which
+// would make it a second round trip).  Returns false if the wave has nothing
+// to do.
 struct GroupMeta {
   int L, r0, G, req;
 };
 __device__ __forceinline__ bool group_meta(const IdxArgs& a, int g, int pi, GroupMeta& m) {
-  const int L = a.lens[g];
-  m.req = a.reqs[g];
+  int L = a.lens[g];
+  int req = a.reqs[g];
   int r0 = g * a.uniform_g, r1 = r0 + a.uniform_g;
   if (a.offs) {
     r0 = a.offs[g];
     r1 = a.offs[g + 1];
   }
+  asm volatile("" : "+s"(L), "+s"(req), "+s"(r0), "+s"(r1));
+  m.req = req;
   m.L = L < a.max_context ? L : a.max_context;
   m.r0 = r0;
   m.G = r1 - r0;
@@ -86,6 +91,8 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       kb[s][ks] = ldg<v8bf>(keys + (16 * s + r) * 128 + 32 * ks + 8 * kg);
+  // every key load is issued before the first product waits for one
+  __builtin_amdgcn_sched_barrier(0);
 
   if (r >= m.G) {
 #pragma unroll
@@ -145,37 +152,55 @@ __device__ __forceinline__ void dequant_row(const v4i& packed, uint32_t scales2,
   for (int ks = 0; ks < 4; ++ks) out[ks] = dequant8((uint32_t)packed[ks], ks < 2 ? s0 : s1);
 }
 
+// One wavefront per (group, run of P pages): the group's length, request and
+// rows are read once for P pages, then the P block-table entries, then every
+// page's keys and scales at once, so a wave pays the chain of dependent
+// reads (length, page id, keys) once per P pages.  Pages of the run at or
+// beyond the length read page 0 instead (every load is issued the same way,
+// and nothing of theirs is stored).
+template <int P>
 __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
   const int g = blockIdx.y;
-  const int pi = blockIdx.x;
+  const int pi0 = blockIdx.x * P;
   const int lane = threadIdx.x;
   GroupMeta m;
-  if (!group_meta(a, g, pi, m)) return;
+  if (!group_meta(a, g, pi0, m)) return;
+  // pages pi0 .. pi0 + np - 1 hold keys below the length (np >= 1)
+  const int np = min(P, (m.L - pi0 * kPage + kPage - 1) / kPage);
 
-  bool bad = (unsigned)m.req >= (unsigned)a.num_requests;
-  const int pg = bad ? 0 : a.bt[(long long)m.req * a.bt_stride + pi];
+  const bool req_bad = (unsigned)m.req >= (unsigned)a.num_requests;
+  int pg[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    pg[p] = (!req_bad && p < np) ? a.bt[(long long)m.req * a.bt_stride + pi0 + p] : 0;
 
   // The query row (lanes past the group's rows read its first row and use
-  // zeros) and, once the page id is known, all four key tiles, each load
-  // issued before any is waited for.
+  // zeros) and, once the page ids are known, all key tiles of the run, each
+  // load issued before any is waited for.
   const int kg = lane >> 4, r = lane & 15;
   const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
   const long long qrow = m.r0 + (r < m.G ? r : 0);
   const v4i qpacked = ldg<v4i>(q8 + qrow * 64 + 16 * kg);
   const uint32_t qsc = *reinterpret_cast<const uint16_t*>(a.qs + qrow * 8 + 2 * kg);
 
-  bad = bad || (unsigned)pg >= (unsigned)a.num_pages;
-  const long long page_id = bad ? 0 : pg;
-  const uint8_t* page = a.kc + page_id * a.page_stride;
-  const uint8_t* pscale = a.ks + page_id * a.scale_page_stride;
-  v4i kpacked[4];
-  uint32_t ksc[4];
+  bool bad[P];
+  v4i kpacked[P][4];
+  uint32_t ksc[P][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int key = 16 * s + r;
-    kpacked[s] = ldg<v4i>(page + key * 64 + 16 * kg);
-    ksc[s] = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
+  for (int p = 0; p < P; ++p) {
+    bad[p] = req_bad || (unsigned)pg[p] >= (unsigned)a.num_pages;
+    const long long page_id = bad[p] ? 0 : pg[p];
+    const uint8_t* page = a.kc + page_id * a.page_stride;
+    const uint8_t* pscale = a.ks + page_id * a.scale_page_stride;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int key = 16 * s + r;
+      kpacked[p][s] = ldg<v4i>(page + key * 64 + 16 * kg);
+      ksc[p][s] = *reinterpret_cast<const uint16_t*>(pscale + key * 8 + 2 * kg);
+    }
   }
+  // every load of the run is issued before the first dequantisation waits
+  __builtin_amdgcn_sched_barrier(0);
 
   v8bf qa[4];
   dequant_row(qpacked, qsc, qa);
@@ -183,26 +208,36 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8bf){};
   }
-  v4f acc[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    v8bf kb[4];
-    dequant_row(kpacked[s], ksc[s], kb);
-    acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < P; ++p) {
+    if (p >= np) break;
+    v4f acc[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
+    for (int s = 0; s < 4; ++s) {
+      v8bf kb[4];
+      dequant_row(kpacked[p][s], ksc[p][s], kb);
+      acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
+    }
+    store_scores(a, m, pi0 + p, lane, bad[p], acc);
   }
-  store_scores(a, m, pi, lane, bad, acc);
 }
 
+// One page per wave: runs of 2 or 4 pages hold 2-4x the registers and were
+// measured slower (8192 rows: 89 and 95 us against 76 us), the waves per SIMD
+// falling from 5-6 to 3-4.
+constexpr int kNvfp4PagesPerWave = 1;
+
 hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream) {
-  dim3 grid(a.max_context / kPage, a.groups);
-  hipLaunchKernelGGL(indexer_nvfp4_kernel, grid, dim3(64), 0, stream, a);
+  constexpr int P = kNvfp4PagesPerWave;
+  dim3 grid((a.max_context / kPage + P - 1) / P, a.groups);
+  hipLaunchKernelGGL(indexer_nvfp4_kernel<P>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
 const void* indexer_nvfp4_kernel_symbol() {
-  return reinterpret_cast<const void*>(&indexer_nvfp4_kernel);
+  return reinterpret_cast<const void*>(&indexer_nvfp4_kernel<kNvfp4PagesPerWave>);
 }
 
 hipError_t launch_indexer(const IdxArgs& a, hipStream_t stream) {
