@@ -244,6 +244,17 @@ def test_indexer_nvfp4_config(uniform):
     check_indexer(di, di.run(), "nvfp4 indexer uniform=%s" % uniform)
 
 
+@pytest.mark.parametrize("name", ["indexer_bf16_8k", "indexer_nvfp4_8k"])
+def test_indexer_8192_rows_dense(name):
+    """The bandwidth-sized indexer workloads the bench times (8192 query rows in
+    groups of 1..8 over 512 requests of 64 pages), every written cell against
+    the dense oracle."""
+    ix = synth.make_config(name)
+    say("%s groups=%d rows=%d" % (name, ix.groups, ix.rows))
+    di = DevIndexer(ix)
+    check_indexer(di, di.run(), name)
+
+
 def test_indexer_nvfp4_fused_pages():
     """Keys and scales as two views of one cache holding each page's keys and
     then their scales (page stride a multiple of 16, not of the key size):
