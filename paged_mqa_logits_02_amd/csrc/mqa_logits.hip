@@ -405,6 +405,11 @@ __device__ __forceinline__ void score_page(const QueryFrag<TW, VAR>& qf,
   for (int si = 0; si < SW; ++si) {
     Frag<VAR> kf;
     kf.load_stage(stage, 16 * (s0 + si) + rr, g);
+    // The widening and the matrix products of a sub-tile run at raised wave
+    // priority, the rectified head sums at the normal one: a wave that has
+    // products ready is issued first and keeps the matrix pipe fed, and the
+    // other waves' head sums fill the vector issue slots in between.
+    __builtin_amdgcn_s_setprio(1);
     const auto kop = key_operand(kf);
     // all matrix products of the sub-tile first, then the rectified head sums
     v4f acc[TW][4];
@@ -412,6 +417,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<TW, VAR>& qf,
     for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mma(qf.op[mt][t], kop);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       // two independent partial sums shorten the dependent FMA chain
