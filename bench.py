@@ -19,6 +19,8 @@ Prints one JSON line (rank 0, one GPU).  Usage:
   python bench.py [--steps K] [--warmup W] [--workload verify_fp8|decode_fp8|mxfp4|...]
                   [--mode in_call|schedule] [--graph|--launch-events] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain copy of known size (counter scale)
+  python bench.py --read-calibration     # page-gather read rate (pages of 8448 / 4352 / 16384 B)
+  python bench.py --gemm-calibration     # library bf16 GEMM (engine clock, matrix rate)
 """
 import argparse
 import json
@@ -216,6 +218,49 @@ def copy_calibration(steps):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": dt * 1e3,
                       "gb_per_s": 2 * n / dt / 1e9}))
+
+
+def read_calibration(steps):
+    """The page-gather read rate of the GPU: whole pages of the logits and
+    indexer kernels' sizes (FP8 8448 B, MXFP4 4352 B, BF16 indexer 16 KiB)
+    read in a random order from a 2 GiB pool by a kernel that does nothing
+    else (libpmqa_calib.so, a measurement tool), one JSON line per size."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_mqa_logits_02_amd", "libpmqa_calib.so"))
+    fn = lib.pmqa_calib_read_pages
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pool.fill_(1)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 16 * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    for page_bytes, per_cu in [(b, g) for b in (8448, 4352, 16384) for g in (4, 16)]:
+        grid = cus * per_cu  # workgroups resident at once, or queued behind them
+        n = pool.numel() // page_bytes
+        ids = torch.randperm(n, generator=gen).to(torch.int32).to(dev)
+
+        def run():
+            rc = fn(pool.data_ptr(), page_bytes, page_bytes, ids.data_ptr(), n, out.data_ptr(),
+                    grid, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("pmqa_calib_read_pages failed (%d)" % rc)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            run()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        dt = ev[0].elapsed_time(ev[1]) / 1e3 / steps
+        print(json.dumps({"page_bytes": page_bytes, "pages": n, "grid": grid,
+                          "ms": dt * 1e3, "gb_per_s": n * page_bytes / dt / 1e9}))
 
 
 def gemm_calibration(steps):
@@ -424,6 +469,7 @@ def main():
                          "workgroups that finish first take the call's last items in chunks")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--gemm-calibration", action="store_true")
+    ap.add_argument("--read-calibration", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -438,6 +484,9 @@ def main():
         return
     if args.gemm_calibration:
         gemm_calibration(args.steps)
+        return
+    if args.read_calibration:
+        read_calibration(args.steps)
         return
 
     import synth

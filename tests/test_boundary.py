@@ -175,3 +175,27 @@ def test_schedule_validation(pm):
     assert lib.mqa_logits_schedule(FAKE, 4, 1, 0, 256, 8, None, None) == NULL
     assert lib.mqa_logits_schedule(FAKE + 2, 4, 1, 0, 256, 8, FAKE, None) == ALIGN
     assert lib.mqa_logits_num_units(0, 9, 0) == UNSUP
+
+
+def test_read_calibration_library_rejects_bad_arguments(pm):
+    """The page-gather read-rate kernel of bench.py --read-calibration lives in
+    its own library; its argument checks run before any launch."""
+    path = os.path.join(ROOT, "paged_mqa_logits_02_amd", "libpmqa_calib.so")
+    if not os.path.exists(path):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = ctypes.CDLL(path)
+    fn = lib.pmqa_calib_read_pages
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    good = dict(pool=FAKE, stride=8448, size=8448, ids=FAKE, n=4, out=FAKE, grid=4)
+    for bad in (dict(pool=None), dict(ids=None), dict(out=None), dict(n=0), dict(grid=0),
+                dict(size=8), dict(size=8450), dict(size=40000, stride=40000),
+                dict(stride=8000), dict(stride=8456)):
+        a = dict(good, **bad)
+        assert fn(a["pool"], a["stride"], a["size"], a["ids"], a["n"], a["out"], a["grid"],
+                  None) == -1, bad
+    out = __import__("subprocess").run(["nm", "-D", pm.LIB_PATH], capture_output=True,
+                                       text=True).stdout
+    assert "pmqa_calib" not in out  # not part of the logits library
