@@ -51,9 +51,15 @@ int limit_by_lds(const DeviceInfo& d, int occ, size_t static_lds, size_t dyn_lds
   return occ;
 }
 
+// MXFP4 kernels keep at most 6 workgroups per CU: the token-record layout with
+// bf16 output fits 7 by its registers and LDS and ran 88.8 us against 82-84 us
+// at 6 (B=64, next_n 2); the trailing-code layout ran the same at 6 and 7.
+constexpr int kMxMaxBlocksPerCu = 6;
+
 int blocks_per_cu(const DeviceInfo& d, int slots, int variant, int out, size_t dyn_lds) {
-  return limit_by_lds(d, d.occ[slots - 1][variant][out], d.static_lds[slots - 1][variant][out],
-                      dyn_lds);
+  const int r = limit_by_lds(d, d.occ[slots - 1][variant][out],
+                             d.static_lds[slots - 1][variant][out], dyn_lds);
+  return variant != 0 && r > kMxMaxBlocksPerCu ? kMxMaxBlocksPerCu : r;
 }
 
 int blocks_per_cu_any(const DeviceInfo& d, int ks, int out, size_t dyn_lds) {

@@ -63,14 +63,14 @@ template <int KS> struct PlaneLayout {
     o.scale = kPage * D + 64 * wave + 4 * (lane & 15);
     return o;
   }
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, Lanes& o, int wave,
                                int lane) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        dma16_page(page + o.key[ks][i], stage + ks * kPlaneBytes + 8 * (2 * wave + i) * 128);
-    if (lane < 16) dma4_page(page + o.scale, stage + kKeyBytes + 64 * wave);
+        dma16_page(page, o.key[ks][i], stage + ks * kPlaneBytes + 8 * (2 * wave + i) * 128);
+    if (lane < 16) dma4_page(page, o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 
@@ -224,7 +224,7 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
   const int B = a.batch;
   const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int Hp = heads_padded(a.heads);
-  const typename L::Lanes dma_lanes = L::lanes(wave, lane, a.head_dim);
+  typename L::Lanes dma_lanes = L::lanes(wave, lane, a.head_dim);
   const int g = lane >> 4;
   const bool partial = a.head_dim < 128 * KS;
   const bool lo_ok = 16 * (8 * (KS - 1) + g) < a.head_dim;

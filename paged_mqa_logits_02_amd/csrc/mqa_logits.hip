@@ -122,14 +122,14 @@ template <int SFV, bool REC> struct MxPageLayout {
     }
     return o;
   }
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, Lanes& o, int wave,
                                int lane) {
     if constexpr (!REC) {
-      dma16_page(page + o.off[0], stage + 16 * wave * kRowBytes);
-      if (lane < kCodeDwords) dma4_page(page + o.off[1], stage + kKeyBytes + 16 * wave * kCodes);
+      dma16_page(page, o.off[0], stage + 16 * wave * kRowBytes);
+      if (lane < kCodeDwords) dma4_page(page, o.off[1], stage + kKeyBytes + 16 * wave * kCodes);
     } else {
-      dma16_page(page + o.off[0], stage + 16 * wave * kRecBytes);
-      if (lane < kTailPieces) dma16_page(page + o.off[1], stage + 16 * wave * kRecBytes + 1024);
+      dma16_page(page, o.off[0], stage + 16 * wave * kRecBytes);
+      if (lane < kTailPieces) dma16_page(page, o.off[1], stage + 16 * wave * kRecBytes + 1024);
     }
   }
 };
@@ -440,8 +440,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<TW, VAR>& qf,
     for (int t = 0; t < TW; ++t) {
       float v = row_transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
       v *= stage_scale<VAR>(stage, lane);
-      store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + lane, v,
-                        valid);
+      store_logit_at<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0, lane, v, valid);
     }
   } else if constexpr (SW == 2) {
     // rows 0-1 end with sub-tile s0, rows 2-3 with s0+1
@@ -456,8 +455,8 @@ __device__ __forceinline__ void score_page(const QueryFrag<TW, VAR>& qf,
       const int token = 16 * (s0 + (lane >> 5)) + rr;
       v *= stage_scale<VAR>(stage, token);
       if ((g & 1) == 0)
-        store_logit<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0 + token, v,
-                          valid);
+        store_logit_at<OUTT>(a.out, row_of(a, b, t0 + t) * a.out_row_stride + col0, token, v,
+                             valid);
     }
   } else {
     static_assert(TW == 1 && SW == 1, "unsupported split");
@@ -465,7 +464,7 @@ __device__ __forceinline__ void score_page(const QueryFrag<TW, VAR>& qf,
     const int token = 16 * s0 + rr;
     v *= stage_scale<VAR>(stage, token);
     if (g == 0)
-      store_logit<OUTT>(a.out, row_of(a, b, t0) * a.out_row_stride + col0 + token, v, valid);
+      store_logit_at<OUTT>(a.out, row_of(a, b, t0) * a.out_row_stride + col0, token, v, valid);
   }
 }
 
@@ -687,15 +686,17 @@ __device__ __forceinline__ void score_page(const RedQuery<TW, VAR>& qf, const ui
       swap16(x2, x3);  // x2 rows: sub-tile 2, sub-tile 3, -, -
       swap32(x0, x2);  // x0 rows: sub-tiles 0, 1, 2, 3
       const int token = 16 * s0 + lane;
-      store_logit<OUTT>(a.out, row + token, x0 * stage_scale<VAR>(stage, token), valid);
+      store_logit_at<OUTT>(a.out, row, token, x0 * stage_scale<VAR>(stage, token), valid);
     } else if constexpr (SW == 2) {
       float x0 = r[0][t], x1 = r[1][t];
       swap16(x0, x1);  // x0 rows: sub-tile 0, sub-tile 1, -, -
       const int token = 16 * s0 + lane;
-      if (lane < 32) store_logit<OUTT>(a.out, row + token, x0 * stage_scale<VAR>(stage, token), valid);
+      if (lane < 32)
+        store_logit_at<OUTT>(a.out, row, token, x0 * stage_scale<VAR>(stage, token), valid);
     } else {
       const int token = 16 * s0 + rr;
-      if (g == 0) store_logit<OUTT>(a.out, row + token, r[0][t] * stage_scale<VAR>(stage, token), valid);
+      if (g == 0)
+        store_logit_at<OUTT>(a.out, row, token, r[0][t] * stage_scale<VAR>(stage, token), valid);
     }
   }
 }
@@ -760,10 +761,17 @@ struct PageFeed {
   __device__ __forceinline__ bool valid(int n) const { return (valid_bits >> (n & 31)) & 1u; }
   __device__ __forceinline__ void issue_next() {
     if (issued >= count) return;
-    const bool ok = page_ok(a, pid_next);
-    const uint8_t* page = a.kv + (long long)(ok ? pid_next : 0) * a.page_stride;
+    // ok = 1 if 0 <= pid < num_pages, from integer arithmetic on the scalar
+    // unit (a comparison result is a lane mask, which costs a vector select
+    // and a read-back to shift into valid_bits): for pid >= 0, pid - num_pages
+    // is negative exactly when pid < num_pages; a negative pid has its sign
+    // bit set, so ~pid clears the result.
+    const uint32_t pid = (uint32_t)pid_next;
+    const uint32_t ok = ((pid - (uint32_t)a.num_pages) & ~pid) >> 31;
+    const uint8_t* page =
+        a.kv + (unsigned long long)(pid & (0u - ok)) * (unsigned long long)a.page_stride;
     L::issue(stage(issued), page, lanes, wave, lane);
-    valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
+    valid_bits = (valid_bits & ~(1u << (issued & 31))) | (ok << (issued & 31));
     ++issued;
     if (issued < count) {
       if ((unsigned)issued % kPidTable == 0) {
@@ -838,7 +846,12 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
     const int pages = min(count - n, tiles_at(s_prefix, b) - j);
     for (int k = 0; k < pages; ++k, ++n, ++j) {
       feed.issue_next();
-      wait_page<L::kLoadsPerWave, kAhead>(feed.issued - n - 1);
+      // kAhead pages were issued after page n, except in the last kAhead
+      // iterations of the range
+      if (n + kAhead < count)
+        wait_vmcnt<kAhead * L::kLoadsPerWave>();
+      else
+        wait_page<L::kLoadsPerWave, kAhead - 1>(feed.issued - n - 1);
       if constexpr (kShared) ring_barrier();  // every wave's share of page n has landed
       if (has_slot)
         score_page<N, OUTT>(qf, feed.stage(n), a, b, j, feed.valid(n), t0, s0, lane);

@@ -3,6 +3,8 @@
 // the FP8 key-page layout and operand fragment, and the page-id table.
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "pmqa_internal.h"
 
@@ -104,12 +106,22 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
 // to HBM land in between the page reads; evict-first page lines leave the
 // output lines cached (measured: 3% faster on long FP8 workloads, 6% on short
 // ones, 11% with few heads; no change in the HBM bytes read).
+//
+// The page base is wave-uniform and each lane adds a 32-bit offset that stays
+// the same from page to page.  The empty asm redefines the caller's offset
+// variable in place at every load, so its zero extension stays next to the
+// load (a loop-invariant offset would be hoisted as a 64-bit value and added
+// to the base with a 64-bit vector add per load) and the load takes the base
+// from scalar registers and the offset from one vector register, with no
+// copy of it.
 constexpr int kPolicyStream = 2;  // cache-policy operand: NT
-__device__ __forceinline__ void dma16_page(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 16, 0, kPolicyStream);
+__device__ __forceinline__ void dma16_page(const uint8_t* page, uint32_t& off, uint8_t* lds_base) {
+  asm volatile("" : "+v"(off));
+  __builtin_amdgcn_global_load_lds(page + off, (lds_void_ptr)lds_base, 16, 0, kPolicyStream);
 }
-__device__ __forceinline__ void dma4_page(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_base, 4, 0, kPolicyStream);
+__device__ __forceinline__ void dma4_page(const uint8_t* page, uint32_t& off, uint8_t* lds_base) {
+  asm volatile("" : "+v"(off));
+  __builtin_amdgcn_global_load_lds(page + off, (lds_void_ptr)lds_base, 4, 0, kPolicyStream);
 }
 
 // Global loads the compiler does not track: it never inserts a wait for
@@ -179,11 +191,11 @@ template <> struct PageLayout<0> {       // FP8: 64 x 128 B keys, 64 fp32 scales
     o.scale = kKeyBytes + 64 * wave + 4 * (lane & 15);
     return o;
   }
-  __device__ static void issue(uint8_t* stage, const uint8_t* page, const Lanes& o, int wave,
+  __device__ static void issue(uint8_t* stage, const uint8_t* page, Lanes& o, int wave,
                                int lane) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_page(page + o.key[i], stage + 8 * (2 * wave + i) * kRowBytes);
-    if (lane < 16) dma4_page(page + o.scale, stage + kKeyBytes + 64 * wave);
+    for (int i = 0; i < 2; ++i) dma16_page(page, o.key[i], stage + 8 * (2 * wave + i) * kRowBytes);
+    if (lane < 16) dma4_page(page, o.scale, stage + kKeyBytes + 64 * wave);
   }
 };
 
@@ -245,6 +257,25 @@ __device__ __forceinline__ void store_logit(void* out, long long idx, float v, b
     const uint16_t bits = valid ? f32_to_bf16_rne(v) : (uint16_t)0x7FC0u;
     reinterpret_cast<uint16_t*>(out)[idx] = bits;
   }
+}
+
+// The same at element `start + col` of the output, where `start` is
+// wave-uniform and `col` (0 .. 63) the lane's column: as for the page loads,
+// the store then takes its base from scalar registers and a 32-bit offset
+// from one vector register (no 64-bit vector add per store).
+template <int OUTT>
+__device__ __forceinline__ void store_logit_at(void* out, long long start, uint32_t col, float v,
+                                               bool valid) {
+  using T = std::conditional_t<OUTT == 0, uint32_t, uint16_t>;
+  T* const base = reinterpret_cast<T*>(out) + start;
+  uint32_t off = col * (uint32_t)sizeof(T);
+  asm volatile("" : "+v"(off));
+  T bits;
+  if constexpr (OUTT == 0)
+    bits = valid ? __float_as_uint(v) : 0x7FC00000u;
+  else
+    bits = valid ? f32_to_bf16_rne(v) : (uint16_t)0x7FC0u;
+  *reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(base) + off) = bits;
 }
 
 // Values read from LDS are wave-uniform here; saying so keeps the cursors in

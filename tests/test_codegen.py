@@ -38,8 +38,13 @@ SOURCES = [("mqa_logits.hip", "17mqa_logits_kernel", 40),
            ("mqa_any.hip", "21mqa_logits_any_kernel", 4)]
 
 
-@pytest.mark.parametrize("src,kernel,count", SOURCES, ids=[s[0] for s in SOURCES])
-def test_page_loop_has_no_full_drain_before_the_matrix_work(src, kernel, count):
+_ASM = {}
+
+
+def device_asm(src):
+    """gfx950 assembly of one library source, compiled with the library's flags."""
+    if src in _ASM:
+        return _ASM[src]
     import sys
     sys.path.insert(0, ROOT)
     from paged_mqa_logits_02_amd import build
@@ -54,7 +59,13 @@ def test_page_loop_has_no_full_drain_before_the_matrix_work(src, kernel, count):
         r = subprocess.run([cc] + flags + ["--cuda-device-only", "-S", path, "-o", out],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
-        asm = open(out).read()
+        _ASM[src] = open(out).read()
+    return _ASM[src]
+
+
+@pytest.mark.parametrize("src,kernel,count", SOURCES, ids=[s[0] for s in SOURCES])
+def test_page_loop_has_no_full_drain_before_the_matrix_work(src, kernel, count):
+    asm = device_asm(src)
     kernels, bad = drains_before_mfma(asm, kernel)
     assert len(kernels) == count
     assert not bad, "vmcnt(0) before the matrix work in: %s" % sorted(set(bad))
@@ -73,3 +84,28 @@ def test_guard_detects_a_drain():
     assert bad
     _, ok = drains_before_mfma(asm.replace("vmcnt(0)", "vmcnt(6)"))
     assert not ok
+
+
+def vector_addressed_page_loads(asm, kernel="17mqa_logits_kernel"):
+    """Page loads into LDS that take a 64-bit vector address (`..., off`)."""
+    kernels = re.findall(r"^(_ZN4pmqa" + kernel + r"\S+):[^\n]*\n(.*?)^\s+s_endpgm", asm,
+                         re.S | re.M)
+    bad = [name for name, body in kernels
+           if re.search(r"^\s*global_load_lds_dword\S*\s+v\[\d+:\d+\],\s*off", body, re.M)]
+    return kernels, bad
+
+
+def test_page_loads_take_a_scalar_base():
+    """Every page load of the 64-head kernels takes the page base from scalar
+    registers and the lane's 32-bit offset from one vector register: a 64-bit
+    vector address costs a 64-bit vector add per load and two more registers
+    per offset (measured: MXFP4 84 -> 80 us with the scalar-base form)."""
+    kernels, bad = vector_addressed_page_loads(device_asm("mqa_logits.hip"))
+    assert len(kernels) == 40
+    assert not bad, "vector-addressed page loads in: %s" % sorted(set(bad))
+    asm = """_ZN4pmqa17mqa_logits_kernelILi1ELi0ELi0EEEvX:   ; @k
+\tglobal_load_lds_dwordx4 v[2:3], off nt
+\ts_endpgm
+"""
+    assert vector_addressed_page_loads(asm)[1]
+    assert not vector_addressed_page_loads(asm.replace("v[2:3], off", "v2, s[4:5]"))[1]
