@@ -247,10 +247,11 @@ __device__ void process_range_any(const MqaArgs& a, const int* s_prefix, int* s_
   int pid_next = uniform(s_pid[0]);
   auto issue_next = [&]() {
     if (issued < count) {
-      const bool ok = page_ok(a, pid_next);
-      const uint8_t* page = a.kv + (long long)(ok ? pid_next : 0) * a.page_stride;
+      const uint32_t ok = page_ok_bit(a, pid_next);  // an out-of-range id loads page 0
+      const uint8_t* page = a.kv + (unsigned long long)((uint32_t)pid_next & (0u - ok)) *
+                                       (unsigned long long)a.page_stride;
       L::issue(ring + ((unsigned)issued % kAnyStages) * L::kStageBytes, page, dma_lanes, wave, lane);
-      valid_bits = (valid_bits & ~(1u << (issued & 31))) | ((ok ? 1u : 0u) << (issued & 31));
+      valid_bits = (valid_bits & ~(1u << (issued & 31))) | (ok << (issued & 31));
       ++issued;
       if (issued < count) {
         if ((unsigned)issued % kPidTable == 0) {

@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) schedule_kernel(const int32_t* __restrict
   }
   for (int u = threadIdx.x; u <= U; u += blockDim.x) {
     long long f = split_point(u, U, cus, skew, P);
-    int b = (u == U) ? B : locate(s_prefix, B, f);
+    int b = (u == U) ? B : locate_lane(s_prefix, B, f);
     int j = (u == U) ? 0 : (int)(f - s_prefix[b]);
     int32_t* e = sched + kSchedHeader + 3 * u;
     e[0] = b;
@@ -761,15 +761,9 @@ struct PageFeed {
   __device__ __forceinline__ bool valid(int n) const { return (valid_bits >> (n & 31)) & 1u; }
   __device__ __forceinline__ void issue_next() {
     if (issued >= count) return;
-    // ok = 1 if 0 <= pid < num_pages, from integer arithmetic on the scalar
-    // unit (a comparison result is a lane mask, which costs a vector select
-    // and a read-back to shift into valid_bits): for pid >= 0, pid - num_pages
-    // is negative exactly when pid < num_pages; a negative pid has its sign
-    // bit set, so ~pid clears the result.
-    const uint32_t pid = (uint32_t)pid_next;
-    const uint32_t ok = ((pid - (uint32_t)a.num_pages) & ~pid) >> 31;
-    const uint8_t* page =
-        a.kv + (unsigned long long)(pid & (0u - ok)) * (unsigned long long)a.page_stride;
+    const uint32_t ok = page_ok_bit(a, pid_next);  // an out-of-range id loads page 0
+    const uint8_t* page = a.kv + (unsigned long long)((uint32_t)pid_next & (0u - ok)) *
+                                     (unsigned long long)a.page_stride;
     L::issue(stage(issued), page, lanes, wave, lane);
     valid_bits = (valid_bits & ~(1u << (issued & 31))) | (ok << (issued & 31));
     ++issued;
@@ -810,8 +804,10 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
   const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int t0 = (wave / WS) * TW, s0 = (wave % WS) * SW;
   // With next_n = 3 the fourth wave has no slot: it loads its share of every
-  // page and takes part in the page barriers, but scores nothing.
-  const bool has_slot = t0 < N;
+  // page and takes part in the page barriers, but scores nothing.  (When the
+  // waves' slot groups cover exactly N slots, every wave has one, known at
+  // compile time.)
+  const bool has_slot = (4 / WS) * TW <= N || t0 < N;
 
   const long long P = uniform(s_prefix[B]);
   if (f0 < 0 || f0 >= P) return;
@@ -892,8 +888,12 @@ __device__ __forceinline__ int grab_chunk(WorkCounter* ctr, int last_grab, int* 
   return c;
 }
 
+// MXFP4 with one code per 32 values and bf16 output runs at 6 waves per SIMD
+// (at most 80 registers); the attribute keeps small changes elsewhere in the
+// kernel from tipping it to 5.
 template <int N, int VAR, int OUTT>
 __global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu((VAR == 1 || VAR == 3) && OUTT == 1 ? 6 : 1)))
     mqa_logits_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sf,
                       const uint8_t* __restrict__ kv, const float* __restrict__ w,
                       const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bt,

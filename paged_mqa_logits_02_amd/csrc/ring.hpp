@@ -57,12 +57,28 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int ma
 }
 
 // Largest b in [0, B] with prefix[b] <= f.  For 0 <= f < prefix[B] the item f
-// lies in request b at page f - prefix[b].
+// lies in request b at page f - prefix[b].  f is wave-uniform: a binary search
+// narrows [lo, hi] to fewer than 64 entries (prefix[lo] <= f throughout), then
+// every lane tests one entry at once; prefix is non-decreasing, so the lanes
+// whose entry is <= f are lanes 0 .. answer - lo.
 __device__ __forceinline__ int locate(const int* s_prefix, int B, long long f) {
   int lo = 0, hi = B;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
+  while (hi - lo >= kWave) {
+    const int mid = (lo + hi + 1) >> 1;
     if (__builtin_amdgcn_readfirstlane(s_prefix[mid]) <= f) lo = mid; else hi = mid - 1;
+  }
+  const int i = lo + (int)(threadIdx.x & (kWave - 1));
+  const int v = s_prefix[i <= hi ? i : hi];  // every lane reads inside [lo, hi]
+  const unsigned long long le = __ballot(i <= hi && v <= f);
+  return lo + __builtin_popcountll(le) - 1;
+}
+
+// The same for a value of f per lane (a plain binary search per lane).
+__device__ __forceinline__ int locate_lane(const int* s_prefix, int B, long long f) {
+  int lo = 0, hi = B;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_prefix[mid] <= f) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -87,7 +103,15 @@ __device__ __forceinline__ long long split_weight_before(int u, int G, int cus, 
   return c + (long long)(y % per) * (1024 + skew * (R - 1 - 2 * ry) / (R - 1));
 }
 __device__ __forceinline__ long long split_point(int u, int G, int cus, int skew, long long P) {
-  if (skew <= 0 || skew >= 1024 || cus < 8 || cus % 8 != 0 || G % cus != 0 || G / cus < 2) return (long long)u * P / G;
+  if (skew <= 0 || skew >= 1024 || cus < 8 || cus % 8 != 0 || G % cus != 0 || G / cus < 2) {
+    // floor(u * P / G) = u * q + floor(u * r / G) with P = q * G + r, in 32-bit
+    // arithmetic when P < 2^31 and G < 2^16 (u <= G, so u * r < G^2 < 2^32)
+    if (P >= 0 && P < (1ll << 31) && G > 0 && G < (1 << 16) && u >= 0 && u <= G) {
+      const unsigned q = (unsigned)P / (unsigned)G, r = (unsigned)P % (unsigned)G;
+      return (long long)((unsigned)u * q + (unsigned)u * r / (unsigned)G);
+    }
+    return (long long)u * P / G;
+  }
   return split_weight_before(u, G, cus, skew) * P / split_weight_before(G, G, cus, skew);
 }
 
@@ -286,8 +310,14 @@ __device__ __forceinline__ int tiles_at(const int* s_prefix, int b) {
   return uniform(s_prefix[b + 1] - s_prefix[b]);
 }
 
-__device__ __forceinline__ bool page_ok(const MqaArgs& a, int pg) {
-  return (unsigned)pg < (unsigned)a.num_pages;
+// 1 if 0 <= pg < num_pages, else 0, by integer arithmetic on the scalar unit
+// (a comparison result is a lane mask, which costs a vector select and a
+// read-back before it can be shifted into a bit set): for pg >= 0,
+// pg - num_pages is negative exactly when pg < num_pages; a negative pg has
+// its sign bit set, and ~pg clears the result.
+__device__ __forceinline__ uint32_t page_ok_bit(const MqaArgs& a, int pg) {
+  const uint32_t p = (uint32_t)pg;
+  return ((p - (uint32_t)a.num_pages) & ~p) >> 31;
 }
 
 // Waits for the loads of the page scored now, given how many pages were
