@@ -357,6 +357,31 @@ def test_schedule_any_unit_count_bit_identical(variant, next_n):
     check_dense(dm, dm.run(), "mid %s" % variant)
 
 
+def test_schedule_entries_name_each_units_request_and_page():
+    """Each unit entry of a schedule holds (request, page, flat item) of its
+    first item: the request is the last one whose page prefix is <= the item
+    (requests with no pages are skipped), the page the offset into it, and the
+    end entry (request B, page 0).  A regression test: the entries were once
+    computed with a wave-uniform search on per-lane items.  (Layout: 8 header
+    ints, then 3 ints per unit and one end entry.)"""
+    inp = _mid_inputs("fp8", next_n=2)
+    dm = DevMqa(inp)
+    B = len(inp.seq_lens)
+    tiles = np.minimum((inp.seq_lens.astype(np.int64) + 63) // 64, inp.max_context // 64)
+    prefix = np.concatenate([[0], np.cumsum(tiles)])
+    for U in (7, 64, 1000):
+        sched = pm().mqa_logits_schedule(dm.sl, inp.next_n, 0, max_context=inp.max_context,
+                                         num_units=U).cpu().numpy()
+        assert sched[1] == U and sched[5] == B and sched[6] == prefix[-1]
+        e = sched[8:8 + 3 * (U + 1)].reshape(U + 1, 3)
+        f = e[:, 2].astype(np.int64)
+        assert f[0] == 0 and f[-1] == prefix[-1] and np.all(np.diff(f) >= 0)
+        b = np.searchsorted(prefix, f[:-1], side="right") - 1
+        assert np.array_equal(e[:-1, 0], b), U
+        assert np.array_equal(e[:-1, 1], f[:-1] - prefix[b]), U
+        assert list(e[-1, :2]) == [B, 0]
+
+
 def test_schedule_for_other_arguments_is_ignored():
     inp = _mid_inputs("fp8", next_n=2)
     dm = DevMqa(inp)
