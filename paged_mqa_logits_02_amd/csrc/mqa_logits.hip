@@ -731,10 +731,16 @@ __device__ __forceinline__ void load_query_any(RedQuery<TW, VAR>& qf, const MqaA
 // kPidTable items.  A page id out of range is replaced by page 0 for the load
 // (so every item issues the same loads) and its outputs are written as NaN.
 // The page id of the next item to issue is read one item ahead.  Every wave
-// of the workgroup makes the same calls (the refill has barriers).
+// of the workgroup makes the same calls (the table fills have barriers).
+//
+// Start-up: the page ids of the first kFirst items are read straight from the
+// block table with scalar loads (all in flight together), and those pages are
+// issued before the page-id table is filled, so that the first pages travel
+// while the table's block-table loads do.
 template <int VAR>
 struct PageFeed {
   using L = PageLayout<VAR>;
+  static constexpr int kFirst = kStages - 1;  // at most; the pipeline issues kAhead first
   const MqaArgs& a;
   const int* s_prefix;
   int* s_pid;
@@ -743,30 +749,62 @@ struct PageFeed {
   int count, issued, pid_next, wave, lane;
   uint32_t valid_bits;  // bit (item % 32): page id was in range
   typename L::Lanes lanes;
+  int first_pid[kFirst];
 
-  // Fills the first block of page ids (b, j: item f0's request and page).
+  // (b, j): item f0's request and page.
   __device__ __forceinline__ PageFeed(const MqaArgs& a_, const int* s_prefix_, int* s_pid_,
                                       uint8_t* ring_, long long f0_, int count_, int b, int j,
                                       int wave_, int lane_)
       : a(a_), s_prefix(s_prefix_), s_pid(s_pid_), ring(ring_), f0(f0_), f_end(f0_ + count_),
         count(count_), issued(0), pid_next(0), wave(wave_), lane(lane_), valid_bits(0),
         lanes(L::lanes(wave_, lane_)) {
-    fill_pid_table(a, s_prefix, s_pid, f0, f_end, b, j);
-    ring_barrier();
-    pid_next = uniform(s_pid[0]);
+    // the (request, page) of items f0 .. f0+kFirst-1 first (LDS reads), then
+    // their block-table entries (scalar loads, all in flight together)
+    int bk[kFirst], jk[kFirst];
+    int bb = b, jj = j, t = tiles_at(s_prefix, b);
+#pragma unroll
+    for (int k = 0; k < kFirst; ++k) {
+      bk[k] = bb;
+      jk[k] = jj;
+      if (k + 1 < kFirst && ++jj == t) {
+        jj = 0;
+        do {
+          ++bb;
+          t = bb < a.batch ? tiles_at(s_prefix, bb) : 1;
+        } while (t == 0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kFirst; ++k)
+      first_pid[k] = k < count ? a.bt[(long long)bk[k] * a.bt_stride + jk[k]] : 0;
   }
   __device__ __forceinline__ uint8_t* stage(int n) const {
     return ring + ((unsigned)n % kStages) * L::kStageBytes;
   }
   __device__ __forceinline__ bool valid(int n) const { return (valid_bits >> (n & 31)) & 1u; }
-  __device__ __forceinline__ void issue_next() {
-    if (issued >= count) return;
-    const uint32_t ok = page_ok_bit(a, pid_next);  // an out-of-range id loads page 0
-    const uint8_t* page = a.kv + (unsigned long long)((uint32_t)pid_next & (0u - ok)) *
-                                     (unsigned long long)a.page_stride;
+  __device__ __forceinline__ void issue_page(int pid) {
+    const uint32_t ok = page_ok_bit(a, pid);  // an out-of-range id loads page 0
+    const uint8_t* page =
+        a.kv + (unsigned long long)((uint32_t)pid & (0u - ok)) * (unsigned long long)a.page_stride;
     L::issue(stage(issued), page, lanes, wave, lane);
     valid_bits = (valid_bits & ~(1u << (issued & 31))) | (ok << (issued & 31));
     ++issued;
+  }
+  // Issues the first `ahead` items (ahead <= kFirst), then fills the first
+  // block of the page-id table.  (b, j): item f0's request and page.
+  template <int ahead>
+  __device__ __forceinline__ void start(int b, int j) {
+    static_assert(ahead >= 1 && ahead <= kFirst, "start-up depth");
+#pragma unroll
+    for (int k = 0; k < ahead; ++k)
+      if (issued < count) issue_page(first_pid[k]);
+    fill_pid_table(a, s_prefix, s_pid, f0, f_end, b, j);
+    ring_barrier();
+    if (issued < count) pid_next = uniform(s_pid[issued]);
+  }
+  __device__ __forceinline__ void issue_next() {
+    if (issued >= count) return;
+    issue_page(pid_next);
     if (issued < count) {
       if ((unsigned)issued % kPidTable == 0) {
         // next block of page ids; every wave gets here at the same item
@@ -822,8 +860,7 @@ __device__ void process_range(const MqaArgs& a, const int* s_prefix, int* s_pid,
   // page 0, not for every page in flight.
   typename QueryOf<N, VAR, OUTT>::type qf;
   if (has_slot) load_query_any<N>(qf, a, b, t0, lane);
-#pragma unroll
-  for (int k = 0; k < kAhead; ++k) feed.issue_next();
+  feed.template start<kAhead>(b, j);
   wait_page<L::kLoadsPerWave, kAhead>(feed.issued - 1);
   if (has_slot) settle_query(qf);
 
