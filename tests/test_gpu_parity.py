@@ -382,6 +382,18 @@ def test_schedule_entries_name_each_units_request_and_page():
         assert list(e[-1, :2]) == [B, 0]
 
 
+def test_mxfp4_grid_keeps_at_most_six_workgroups_per_cu():
+    """MXFP4 launches one range per resident workgroup and at most 6 per CU
+    (7 fit some layouts by registers and LDS and ran slower); FP8 keeps what
+    its registers and LDS allow."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    for next_n in (1, 2, 3, 4):
+        u = pm().num_units(next_n, 1)
+        assert u % cus == 0 and 1 <= u // cus <= 6, (next_n, u, cus)
+        f = pm().num_units(next_n, 0)
+        assert f % cus == 0 and f // cus >= 1, (next_n, f, cus)
+
+
 def test_schedule_for_other_arguments_is_ignored():
     inp = _mid_inputs("fp8", next_n=2)
     dm = DevMqa(inp)
@@ -598,13 +610,17 @@ def test_prepared_call_matches_direct_call(variant):
 def test_out_of_range_page_id_gives_nan_for_that_page_only(variant):
     """A block-table entry outside [0, num_pages) is never dereferenced: the
     outputs of that page (every slot row of the request, the page's 64
-    columns) are NaN, and every other written cell is as with a valid table."""
+    columns) are NaN, and every other written cell is as with a valid table.
+    (Entries just past the pool, the int32 extremes and a small negative id;
+    a request's first page is among them, which a range may start with.)"""
     inp = _mid_inputs(variant, next_n=2, seed=311)
     tiles = np.where(inp.seq_lens > 0, (inp.seq_lens + 63) // 64, 0)
     b1, b2 = [int(b) for b in np.nonzero(tiles >= 3)[0][:2]]
     bad = copy.copy(inp)
     bad.block_table = inp.block_table.copy()
     bad.block_table[b1, 1] = inp.num_pages + 7
+    bad.block_table[b1, 2] = 2**31 - 1
+    bad.block_table[b2, 0] = -2**31
     bad.block_table[b2, 2] = -5
     out = DevMqa(bad).run()
     got, wrote = host_out(out)
@@ -612,7 +628,8 @@ def test_out_of_range_page_id_gives_nan_for_that_page_only(variant):
     assert np.array_equal(wrote, written)
     N = inp.next_n
     poison = np.zeros_like(written)
-    poison[b1 * N:(b1 + 1) * N, 64:128] = True
+    poison[b1 * N:(b1 + 1) * N, 64:192] = True
+    poison[b2 * N:(b2 + 1) * N, 0:64] = True
     poison[b2 * N:(b2 + 1) * N, 128:192] = True
     assert np.array_equal(poison & written, poison)
     assert np.isnan(got[poison]).all()
