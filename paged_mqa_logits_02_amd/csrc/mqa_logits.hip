@@ -950,11 +950,16 @@ __global__ void __launch_bounds__(256)
   __shared__ int s_pid[kPidTable];
   uint8_t* ring = smem;
   int* s_prefix = reinterpret_cast<int*>(smem + ring_bytes<N, VAR>());
+  // The grid size (a hidden kernel argument), the split parameters and the
+  // query's address are read with the first batch of argument loads: read
+  // where they are first needed, after the prefix's global loads, each batch
+  // would be one more round trip to the arguments before the first page.
+  const int G = gridDim.x;
+  asm volatile("" ::"s"(G), "s"(q), "s"(dims.cus), "s"(dims.split_skew));
   build_prefix(a.seq_lens, a.batch, a.max_context / kPage, s_prefix, s_wsum);
 
   // Consecutive units on one XCD: workgroups are dealt to the 8 XCDs
   // round-robin, so renumber them XCD-major before splitting the work.
-  const int G = gridDim.x;
   const int unit = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   // The schedule header is read at once (no short-circuit between its

@@ -23,14 +23,19 @@ __device__ __forceinline__ int tiles_of(int L, int max_tiles) {
 }
 
 // Exclusive prefix of per-request page counts into s_prefix[0..B]
-// (s_prefix[B] = total).  Whole workgroup; ends with a barrier.
+// (s_prefix[B] = total).  Whole workgroup of kBlockThreads threads; ends with
+// a barrier.
 __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int max_tiles,
                              int* s_prefix, int* s_wsum) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x, nthr = kBlockThreads;
   const int lane = tid & (kWave - 1), wave = tid / kWave, nwave = nthr / kWave;
   const int per = (B + nthr - 1) / nthr;
   const int lo = tid * per;
   const int hi = min(lo + per, B);
+  // seq_lens's address is wanted here, before the per-thread branch: read
+  // there, it would be a second round trip to the kernel arguments after the
+  // one that brings B, before the first global load of the launch.
+  asm volatile("" ::"s"(seq_lens));
   int sum = 0;
   for (int i = lo; i < hi; ++i) {
     int t = tiles_of(seq_lens[i], max_tiles);
@@ -57,10 +62,11 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int ma
 }
 
 // Largest b in [0, B] with prefix[b] <= f.  For 0 <= f < prefix[B] the item f
-// lies in request b at page f - prefix[b].  f is wave-uniform: a binary search
-// narrows [lo, hi] to fewer than 64 entries (prefix[lo] <= f throughout), then
-// every lane tests one entry at once; prefix is non-decreasing, so the lanes
-// whose entry is <= f are lanes 0 .. answer - lo.
+// lies in request b at page f - prefix[b].  f is wave-uniform and all 64 lanes
+// of the wave call it: a binary search narrows [lo, hi] to fewer than 64
+// entries (prefix[lo] <= f throughout), then every lane tests one entry at
+// once; prefix is non-decreasing, so the lanes whose entry is <= f are lanes
+// 0 .. answer - lo.
 __device__ __forceinline__ int locate(const int* s_prefix, int B, long long f) {
   int lo = 0, hi = B;
   while (hi - lo >= kWave) {
