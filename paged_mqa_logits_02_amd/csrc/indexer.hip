@@ -113,41 +113,36 @@ __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
 // The same contraction with NVFP4 query rows and keys: packed e2m1, an e4m3
 // scale per 16 values (query_scales [rows, 8]; key_scales [pages, 64, 8],
 // paged like the keys).  An e2m1 value times an e4m3 scale has at most six
-// significant bits, so each side is dequantised exactly into bf16 registers and
-// the bf16 MFMA computes the products exactly, accumulating in fp32.
+// significant bits, so each side is dequantised exactly into f16 registers and
+// the f16 MFMA computes the products exactly, accumulating in fp32.
 //
 // K mapping: lane (kg = l>>4) holds, in K step ks, head_dim values
 // 32kg + 8ks .. 32kg + 8ks + 7, the same for query and key, so the four K
 // steps of a lane are one contiguous 16-byte slice of a packed row and two of
 // its scales (blocks 2kg and 2kg+1).
 
-// Eight dequantised values (one packed dword, scale s) as bf16.
-typedef float v2f __attribute__((ext_vector_type(2)));
-
-// Two e2m1 values of byte B of `packed` (low nibble first) times s, as bf16;
-// exact (the conversion applies only a power-of-two scale, so s is applied
-// by a separate fp32 multiply).
+// Two e2m1 values of byte B of `packed` (low nibble first) times s, as f16.
+// The conversion applies only a power-of-two scale, so it runs with scale 1
+// and s (the block's e4m3 scale in both halves) is applied by a packed f16
+// multiply.  Exact: the product has at most six significant bits and is 0 or
+// of magnitude 2^-10 .. 6 * 448, inside f16's normal range.
 template <int B>
-__device__ __forceinline__ void dequant2(uint32_t packed, float s, v8bf& r) {
-  const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, B);
-  r[2 * B] = (__bf16)(f[0] * s);
-  r[2 * B + 1] = (__bf16)(f[1] * s);
+__device__ __forceinline__ v2h dequant2(uint32_t packed, v2h s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, B) * s;
 }
 
-__device__ __forceinline__ v8bf dequant8(uint32_t packed, float s) {
-  v8bf r;
-  dequant2<0>(packed, s, r);
-  dequant2<1>(packed, s, r);
-  dequant2<2>(packed, s, r);
-  dequant2<3>(packed, s, r);
-  return r;
+// Eight dequantised values (one packed dword, scale s).
+__device__ __forceinline__ v8h dequant8(uint32_t packed, v2h s) {
+  const v2h a = dequant2<0>(packed, s), b = dequant2<1>(packed, s);
+  const v2h c = dequant2<2>(packed, s), d = dequant2<3>(packed, s);
+  return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// A lane's 32 values of one NVFP4 row (16 packed bytes, two e4m3 scales) as
-// the four K-step fragments.
-__device__ __forceinline__ void dequant_row(const v4i& packed, uint32_t scales2, v8bf out[4]) {
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)scales2, 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)scales2, 1);
+// A lane's 32 values of one NVFP4 row (16 packed bytes, two e4m3 scales, each
+// widened exactly to f16) as the four K-step fragments.
+__device__ __forceinline__ void dequant_row(const v4i& packed, uint32_t scales2, v8h out[4]) {
+  const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)scales2, 1.0f, false);
+  const v2h s0 = (v2h){sc[0], sc[0]}, s1 = (v2h){sc[1], sc[1]};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) out[ks] = dequant8((uint32_t)packed[ks], ks < 2 ? s0 : s1);
 }
@@ -202,11 +197,11 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
   // every load of the run is issued before the first dequantisation waits
   __builtin_amdgcn_sched_barrier(0);
 
-  v8bf qa[4];
+  v8h qa[4];
   dequant_row(qpacked, qsc, qa);
   if (r >= m.G) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8bf){};
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = (v8h){};
   }
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -214,19 +209,19 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
     v4f acc[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      v8bf kb[4];
+      v8h kb[4];
       dequant_row(kpacked[p][s], ksc[p][s], kb);
       acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_bf16(qa[ks], kb[ks], acc[s]);
+      for (int ks = 0; ks < 4; ++ks) acc[s] = mfma_f16(qa[ks], kb[ks], acc[s]);
     }
     store_scores(a, m, pi0 + p, lane, bad[p], acc);
   }
 }
 
-// One page per wave: runs of 2 or 4 pages hold 2-4x the registers and were
-// measured slower (8192 rows: 89 and 95 us against 76 us), the waves per SIMD
-// falling from 5-6 to 3-4.
+// One page per wave: runs of 2 or 4 pages hold 2-4x the key registers and were
+// measured slower (8192 rows: 77 us for both against 61 us), the waves per
+// SIMD falling from 7 to 5 and 4.
 constexpr int kNvfp4PagesPerWave = 1;
 
 hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream) {
