@@ -766,3 +766,44 @@ def test_cancelling_dot_product_mxfp4(next_n, dtype, one_hot):
     dm = DevMqa(inp)
     r = check_dense(dm, dm.run(), "cancelling mxfp4 N=%d %s" % (next_n, dtype))
     say("  max err/tol %.3g" % r)
+
+
+def nvfp4_extreme_scale_inputs():
+    """The indexer_nvfp4 workload with every query row reduced to one block of
+    16 values (row r keeps block r mod 8, the rest of its codes zero) and the
+    e4m3 scales of both sides drawn from the format's extremes: the smallest
+    subnormal 2^-9, the largest subnormal 7 * 2^-9, the smallest normal 2^-6,
+    1, the largest finite 448, and negatives.  Each score is then one scale
+    product times a sum of 16 e2m1 products (a multiple of 1/4 of magnitude at
+    most 576), exactly representable in fp32, so the kernel's f16 operands
+    (e2m1 value times scale: 2^-10 .. 2688 in magnitude) and fp32 sums must
+    reproduce the oracle bit for bit."""
+    ix = copy.copy(synth.make_config("indexer_nvfp4"))
+    ext = np.array([0x01, 0x07, 0x08, 0x38, 0x7E, 0x81, 0xFE, 0x3F], dtype=np.uint8)
+    q = ix.query.copy()
+    for r in range(ix.rows):
+        keep = r % 8
+        q[r, :8 * keep] = 0
+        q[r, 8 * keep + 8:] = 0
+    ix.query = q
+    ix.query_scales = ext[(np.arange(ix.rows)[:, None] + np.arange(8)[None, :]) % 8].astype(np.uint8)
+    ks = ix.key_scales.copy()
+    P = ks.shape[0]
+    k = np.arange(64)[None, :, None]
+    j = np.arange(8)[None, None, :]
+    p = np.arange(P)[:, None, None]
+    ks[:, :512] = ext[(3 * k + j + p) % 8].reshape(P, 512)
+    ix.key_scales = ks
+    return ix
+
+
+def test_indexer_nvfp4_extreme_scales_bit_exact():
+    ix = nvfp4_extreme_scale_inputs()
+    ref, _, written = oracle.indexer_scores_for(ix)
+    exp = ref[written]
+    assert np.array_equal(exp.astype(np.float32).astype(np.float64), exp)  # the premise
+    assert np.abs(exp).max() > 1e6 and np.abs(exp[exp != 0]).min() < 1e-5
+    say("nvfp4 indexer extreme scales: %d cells" % int(written.sum()))
+    got, wrote = host_out(DevIndexer(ix).run())
+    assert np.array_equal(wrote, written)
+    assert np.array_equal(got[written], exp.astype(np.float32))
