@@ -212,7 +212,8 @@ int mqa_logits_mxfp4(const void* q, const void* q_sf, int32_t sf_vec_size,
  *   scores           fp32 [rows, scores_row_stride]: scores[r, k] for k below the
  *                    group's length (clamped to max_context) is the dot product
  *                    of query row r with key k; later entries are not written.
- *                    max_context % 64 == 0, scores_row_stride >= max_context.
+ *                    max_context % 64 == 0 and at most 65535 pages (4194240
+ *                    keys), scores_row_stride >= max_context; groups <= 65535.
  */
 int indexer_scores(const void* query, int32_t rows, int32_t head_dim, const void* key_cache,
                    int64_t page_stride, int32_t num_pages, const int32_t* block_table,

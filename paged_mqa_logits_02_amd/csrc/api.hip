@@ -329,6 +329,7 @@ static int check_indexer(const void* query, int32_t rows, int32_t head_dim, cons
   if (rows < 0 || groups < 0 || groups > 65535 || head_dim < 1) return PMQA_ERR_SHAPE;
   if (head_dim != 128) return PMQA_ERR_UNSUPPORTED;
   if (max_context < 0 || max_context % PMQA_PAGE_TOKENS != 0) return PMQA_ERR_SHAPE;
+  if (max_context / PMQA_PAGE_TOKENS > 65535) return PMQA_ERR_SHAPE;  // grid.y = pages
   if (groups > 0 && rows < 1) return PMQA_ERR_SHAPE;
   *uniform_g = 0;
   if (!group_row_offsets && groups > 0) {

@@ -9,6 +9,14 @@
 // One wavefront per (group, page): the group's 1..8 query rows form the A
 // operand of 16x16x32 bf16 MFMAs (rows padded to 16 with zeros), the page's
 // 64 keys the B operand in four 16-token tiles; head_dim 128 is four K steps.
+//
+// The grid is page-major (x = group, y = page position): the dispatcher hands
+// out every group's page p before any group's page p + 1, so groups that share
+// a request read each of its pages at nearly the same time and all but the
+// first find it in the caches, and the waves past a group's length (which
+// exit at once) are spread over the whole launch instead of ending each
+// group's run.  Measured against the group-major grid at 8192 query rows:
+// BF16 181 -> 137 us, NVFP4 61 -> 51.5 us.
 #include "device.hpp"
 #include "pmqa_internal.h"
 
@@ -58,8 +66,8 @@ __device__ __forceinline__ void store_scores(const IdxArgs& a, const GroupMeta& 
 }
 
 __global__ void __launch_bounds__(64) indexer_kernel(const IdxArgs a) {
-  const int g = blockIdx.y;
-  const int pi = blockIdx.x;
+  const int g = blockIdx.x;
+  const int pi = blockIdx.y;
   const int lane = threadIdx.x;
   GroupMeta m;
   if (!group_meta(a, g, pi, m)) return;
@@ -155,8 +163,8 @@ __device__ __forceinline__ void dequant_row(const v4i& packed, uint32_t scales2,
 // and nothing of theirs is stored).
 template <int P>
 __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
-  const int g = blockIdx.y;
-  const int pi0 = blockIdx.x * P;
+  const int g = blockIdx.x;
+  const int pi0 = blockIdx.y * P;
   const int lane = threadIdx.x;
   GroupMeta m;
   if (!group_meta(a, g, pi0, m)) return;
@@ -220,13 +228,13 @@ __global__ void __launch_bounds__(64) indexer_nvfp4_kernel(const IdxArgs a) {
 }
 
 // One page per wave: runs of 2 or 4 pages hold 2-4x the key registers and were
-// measured slower (8192 rows: 77 us for both against 61 us), the waves per
-// SIMD falling from 7 to 5 and 4.
+// measured slower (8192 rows, group-major grid: 77 us for both against
+// 61 us), the waves per SIMD falling from 7 to 5 and 4.
 constexpr int kNvfp4PagesPerWave = 1;
 
 hipError_t launch_indexer_nvfp4(const IdxArgs& a, hipStream_t stream) {
   constexpr int P = kNvfp4PagesPerWave;
-  dim3 grid((a.max_context / kPage + P - 1) / P, a.groups);
+  dim3 grid(a.groups, (a.max_context / kPage + P - 1) / P);
   hipLaunchKernelGGL(indexer_nvfp4_kernel<P>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
@@ -236,7 +244,7 @@ const void* indexer_nvfp4_kernel_symbol() {
 }
 
 hipError_t launch_indexer(const IdxArgs& a, hipStream_t stream) {
-  dim3 grid(a.max_context / kPage, a.groups);
+  dim3 grid(a.groups, a.max_context / kPage);
   hipLaunchKernelGGL(indexer_kernel, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }

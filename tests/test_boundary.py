@@ -136,6 +136,7 @@ def _idx(lib, **kw):
 @pytest.mark.parametrize("kw,rc", [
     (dict(D=64), UNSUP), (dict(groups=5), SHAPE), (dict(groups=2), SHAPE),
     (dict(groups=65536, rows=65536), SHAPE), (dict(maxc=4000), SHAPE),
+    (dict(maxc=65536 * 64, btw=65536, bts=65536, srs=65536 * 64), SHAPE),
     (dict(ps=16384 - 16), SHAPE), (dict(ps=16384 + 8), ALIGN), (dict(btw=32), SHAPE),
     (dict(srs=100), SHAPE), (dict(scores=None), NULL), (dict(reqs=None), NULL),
     (dict(q=FAKE + 2), ALIGN), (dict(nreq=0), SHAPE), (dict(groups=0), OK),
@@ -160,7 +161,7 @@ def _idx4(lib, **kw):
     (dict(ps=4096 + 8), ALIGN), (dict(sps=504), SHAPE), (dict(sps=516), ALIGN),
     (dict(qs=None), NULL), (dict(ks=None), NULL), (dict(q=None), NULL),
     (dict(qs=FAKE + 1), ALIGN), (dict(q=FAKE + 8), ALIGN), (dict(btw=32), SHAPE),
-    (dict(groups=0), OK),
+    (dict(maxc=65536 * 64, btw=65536, bts=65536, srs=65536 * 64), SHAPE), (dict(groups=0), OK),
 ])
 def test_indexer_nvfp4_validation(pm, kw, rc):
     assert _idx4(pm.library(), **kw) == rc
